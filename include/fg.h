@@ -1,0 +1,211 @@
+/*
+ * fg.h -- C ABI of libfg.so: ragged paged attention for Dynamic SplitFuse
+ * passes on AMD Instinct MI355X (gfx950).
+ *
+ * A "pass" is one forward step's worth of attention at a fixed token budget:
+ * each sequence s brings q_lens[s] new query tokens (a prompt chunk when > 1,
+ * a decode when == 1) on top of ctx_lens[s] tokens already in a paged KV
+ * cache.  Composing such passes from prompt chunks plus decode tokens is
+ * Dynamic SplitFuse ("DeepSpeed-FastGen: High-throughput Text Generation for
+ * LLMs via MII and DeepSpeed-Inference", research summary page, section
+ * "Summary"; InfoQ news item "Microsoft releases DeepSpeed-FastGen").
+ *
+ * The cache is paged: fixed-size physical blocks addressed per sequence by a
+ * block table that the kernels read themselves ("DeepSpeed-FastGen Guide:
+ * Dynamic SplitKV Serving", section "3. Paged KV Memory Management with Zero
+ * Overhead").  Long KV ranges are split over compute units and the partial
+ * results merged by log-sum-exp (same page, section "1. Dynamic SplitKV
+ * Attention").
+ *
+ * Call order for one pass, all on one HIP stream, nothing synchronises inside
+ * the library:
+ *     fg_plan_pass -> fg_plan_upload -> fg_kv_append -> fg_attention_ragged
+ *     ... stream sync ... -> fg_plan_destroy
+ *
+ * Conventions
+ * -----------
+ * - Every function returns an fg_status (0 = success, negative = error); no
+ *   exception crosses the ABI and nothing aborts.
+ * - All validation happens in fg_plan_pass; a plan that exists is valid, and
+ *   the kernels never see an index outside the pools.
+ * - The library never allocates device memory.  The caller owns every device
+ *   buffer (metadata, workspace, pools, inputs, outputs) and the stream.
+ * - Device pointers must be 16-byte aligned.  `stream` is a hipStream_t passed
+ *   as void* (NULL = the null stream).
+ * - Plans are immutable after fg_plan_pass; functions are reentrant.  Calls
+ *   that write the same device buffers must not overlap in time.
+ * - bf16 means IEEE binary32's upper 16 bits (round-to-nearest-even when the
+ *   library rounds).
+ *
+ * Tensor layouts (row-major, innermost last)
+ * ------------------------------------------
+ *   q          [T, Hq, D]            bf16, tokens in sequence order
+ *   k_new/v_new[T, Hkv, D]           bf16, same token order
+ *   k_pool     [num_blocks, Hkv, B, D]  bf16  (slot-major within a block)
+ *   v_pool     [num_blocks, Hkv, D, B]  bf16  (each block stored transposed:
+ *                                      for every dim, B slots contiguous)
+ *   out        [T, Hq, D]            fp32 or bf16
+ *   lse        [T, Hq]               fp32, natural log
+ * where T = sum(q_lens), B = block_size, D = head_dim.  Token j of sequence s
+ * lives at absolute position p = ctx_lens[s] + j, in physical block
+ * block_tables[s*max_blocks_per_seq + p / B] at slot p % B.  Query head h
+ * reads kv head h / (Hq / Hkv).
+ */
+#ifndef FG_H
+#define FG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FG_ABI_VERSION 1
+
+typedef int32_t fg_status;
+
+enum {
+  FG_OK = 0,
+  FG_E_INVALID = -1,     /* null pointer, negative count, Hq % Hkv != 0, bad knob */
+  FG_E_RANGE = -2,       /* block id outside [0, num_blocks); table row too short
+                            for ctx + q_len; q_len < 1; size overflow */
+  FG_E_ALIAS = -3,       /* a physical block used twice within one pass */
+  FG_E_UNSUPPORTED = -4, /* head_dim not in {64,128}, block_size not in {16,32,64},
+                            unknown output dtype */
+  FG_E_WORKSPACE = -5,   /* workspace smaller than the plan needs, or misaligned */
+  FG_E_HIP = -6,         /* a HIP runtime call or kernel launch failed */
+  FG_E_NOMEM = -7        /* host allocation failed */
+};
+
+enum { FG_DTYPE_F32 = 0, FG_DTYPE_BF16 = 1 };
+
+/* Description of one pass.  All pointers are host pointers; the planner
+ * copies what it needs, so they may be freed when fg_plan_pass returns. */
+typedef struct fg_pass_desc {
+  int32_t num_seqs;           /* S >= 0 (S == 0 is an empty pass) */
+  int32_t num_q_heads;        /* Hq >= 1 */
+  int32_t num_kv_heads;       /* Hkv >= 1, Hq % Hkv == 0 */
+  int32_t head_dim;           /* D: 64 or 128 */
+  int32_t block_size;         /* B: 16, 32 or 64 tokens */
+  int32_t num_blocks;         /* physical blocks in each pool, >= 1 */
+  int32_t max_blocks_per_seq; /* row stride of block_tables */
+  float scale;                /* softmax scale; 0 selects 1/sqrt(D) */
+  const int32_t* q_lens;      /* [S], each >= 1 */
+  const int32_t* ctx_lens;    /* [S], each >= 0 */
+  const int32_t* block_tables;/* [S * max_blocks_per_seq]; entries past
+                                 ceil((ctx+q_len)/B) are ignored, the used ones
+                                 must lie in [0, num_blocks) and be distinct
+                                 across the whole pass */
+  /* Planner knobs (0 = default).  They change speed only, never results. */
+  int32_t target_cus;         /* compute units to balance over; 0 = query the
+                                 current HIP device (needs a GPU) */
+  int32_t min_split_tokens;   /* smallest KV range worth its own work item */
+  int32_t max_splits;         /* cap on KV splits of one row group (<= 256) */
+  int32_t force_splits;       /* > 0: split every row group's KV range into this
+                                 many parts regardless of cost (tests) */
+} fg_pass_desc;
+
+typedef struct fg_plan fg_plan;
+
+typedef struct fg_plan_info_t {
+  int64_t num_tokens;      /* T */
+  int64_t metadata_bytes;  /* size of the device metadata buffer */
+  int64_t workspace_bytes; /* size of the attention workspace (may be 0) */
+  int32_t num_items;       /* attention work items (work-groups) */
+  int32_t num_valu_items;  /* of which on the vector-ALU path (few query rows) */
+  int32_t num_mfma_items;  /* of which on the matrix-core path (row tiles) */
+  int32_t num_merge_groups;/* row groups whose KV range was split */
+  int32_t num_partial_rows;/* partial (O, lse) rows held in the workspace */
+  int32_t max_splits_used;
+  int32_t num_append_runs; /* (sequence, block) runs the append writes */
+  int32_t target_cus;      /* CU count the plan was balanced for */
+} fg_plan_info_t;
+
+/* Build the plan of one pass (host only, no device call unless
+ * desc->target_cus == 0).  Validates every input (see fg_status).  On success
+ * *out_plan receives a plan owned by the library; free it with
+ * fg_plan_destroy.  Deterministic: the same desc gives a byte-identical plan. */
+fg_status fg_plan_pass(const fg_pass_desc* desc, fg_plan** out_plan);
+
+/* Report sizes and counts of a plan. */
+fg_status fg_plan_info(const fg_plan* plan, fg_plan_info_t* out);
+
+/* Copy the plan's metadata into d_meta (device, >= metadata_bytes,
+ * caller-owned) with an asynchronous host-to-device copy on `stream`.  The
+ * plan must stay alive until the stream has passed the copy. */
+fg_status fg_plan_upload(const fg_plan* plan, void* d_meta, void* stream);
+
+/* Scatter the pass's new K and V into their cache slots (asynchronous).
+ * k_new, v_new: [T, Hkv, D] bf16; k_pool, v_pool: pools in the layouts above.
+ * Writes exactly T*Hkv K rows and T*Hkv V columns; no other byte of the pools
+ * changes.  Bit-exact copy. */
+fg_status fg_kv_append(const fg_plan* plan, const void* d_meta,
+                       const void* k_new, const void* v_new,
+                       void* k_pool, void* v_pool, void* stream);
+
+/* Attention of every query row of the pass over its sequence's cached keys
+ * 0 .. ctx + j (inclusive causal bound), read through the block tables
+ * (asynchronous).  The pools must already hold this pass's K/V (append
+ * first, on the same stream).  q: [T, Hq, D] bf16.  out: [T, Hq, D] of
+ * out_dtype (FG_DTYPE_F32 or FG_DTYPE_BF16).  lse: [T, Hq] fp32 or NULL.
+ * d_ws: caller-owned workspace of >= workspace_bytes (may be NULL when that is
+ * 0); its contents on entry do not matter. */
+fg_status fg_attention_ragged(const fg_plan* plan, const void* d_meta,
+                              const void* q, const void* k_pool, const void* v_pool,
+                              void* out, int32_t out_dtype, float* lse,
+                              void* d_ws, size_t ws_bytes, void* stream);
+
+/* Free a plan (NULL is allowed).  Only after the stream has passed every
+ * call that used it. */
+void fg_plan_destroy(fg_plan* plan);
+
+/* Static, human-readable name of a status code. */
+const char* fg_status_string(fg_status status);
+
+/* FG_ABI_VERSION of the built library. */
+int32_t fg_abi_version(void);
+
+/* ---- introspection (tests and debugging) -----------------------------------
+ * Copy the plan's packed device metadata (metadata_bytes; the same bytes
+ * fg_plan_upload sends) into the host buffer host_dst of `bytes` bytes, and
+ * report where each record section starts.  Records are little-endian int32:
+ *   sequence  8 ints: q_start, q_len, ctx, kv_len, block_id_offset, num_blocks, 0, 0
+ *   block id  1 int:  physical block of each used table entry, per sequence
+ *   run       4 ints: first new-token row, first slot, token count, block
+ *   item      8 ints: seq, kv_head, row0, nrows, kv0, kv1, slot (-1 = final
+ *                     rows, else first partial row), waves (0 = vector-ALU path)
+ *   merge     8 ints: seq, kv_head, row0, nrows, nsplit, slot0, 0, 0
+ * Packed row r of an item is query token r / G at q head kv_head * G + r % G;
+ * split i of a merge group's row r sits at partial row slot0 + i * nrows + r.
+ * host_dst may be NULL to query the layout only. */
+typedef struct fg_plan_layout_t {
+  int64_t seqs, block_ids, runs, items, merges;   /* byte offsets */
+  int32_t num_seqs, num_block_ids, num_runs, num_items, num_merges, pad;
+} fg_plan_layout_t;
+
+fg_status fg_plan_metadata(const fg_plan* plan, void* host_dst, size_t bytes,
+                           fg_plan_layout_t* layout);
+
+/* ---- measurement hooks ------------------------------------------------------
+ * When enabled, the library brackets each of its kernel launches with HIP
+ * events recorded on the launch stream.  fg_profile_read waits for the
+ * recorded events, writes per-kernel totals (milliseconds and launch counts,
+ * indexed by the FG_KERNEL_* ids) and clears the record.  Off by default; the
+ * record is process-wide and not thread-safe. */
+enum {
+  FG_KERNEL_APPEND = 0,
+  FG_KERNEL_ATTENTION = 1,
+  FG_KERNEL_MERGE = 2,
+  FG_KERNEL_COUNT = 3
+};
+
+fg_status fg_profile_enable(int32_t on);
+fg_status fg_profile_read(double* total_ms, int32_t* launches, int32_t n_kernels);
+const char* fg_kernel_name(int32_t kernel_id);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FG_H */

@@ -1,0 +1,795 @@
+// fg_device.hip -- gfx950 kernels of one ragged paged attention pass and the
+// C-ABI entry points that launch them.
+//
+// Kernels
+//   append_kernel   one work-group per (append run, kv head): copies the new K
+//                   rows into their block (slot-major) and writes the new V
+//                   rows transposed into the block's [D][B] layout through LDS.
+//   attn_kernel     one work-group per work item.  Items with many query rows
+//                   (prompt-chunk tiles, GQA groups) take the matrix-core path:
+//                   K/V stages of 64 tokens staged in LDS, S^T = K Q^T and
+//                   O^T = V^T P^T on v_mfma_f32_32x32x16_bf16, online softmax in
+//                   fp32 with one query row per lane.  Items with at most four
+//                   rows (decodes) take the vector-ALU path: every wavefront
+//                   streams its own 32-token sub-tiles with 16-byte loads,
+//                   dot products on v_dot2_f32_bf16 with DPP row reductions, and
+//                   the four wavefronts merge by log-sum-exp at the end.
+//   merge_kernel    log-sum-exp merge of split partials ("DeepSpeed-FastGen
+//                   Guide: Dynamic SplitKV Serving", section "1. Dynamic SplitKV
+//                   Attention", two-phase softmax item; the weights are the
+//                   partials' log-sum-exp values).
+//
+// Exponentials run base 2 on v_exp_f32 with the softmax scale folded into
+// scale * log2(e); log-sum-exp values are returned in natural-log units.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <mutex>
+#include <vector>
+
+#include "fg.h"
+#include "fg_meta.h"
+#include "plan.h"
+
+namespace fg {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+
+struct AttnArgs {
+  const SeqRec* seqs;
+  const int32_t* bt;
+  const ItemRec* items;
+  const uint16_t* q;
+  const uint16_t* kpool;
+  const uint16_t* vpool;
+  void* out;
+  float* lse;
+  float* ws_o;
+  float* ws_lse;
+  int32_t hq, hkv, group, n_mfma;
+  float scale_log2;  // softmax scale * log2(e)
+  int32_t out_bf16;
+};
+
+__device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void st16(uint16_t* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of LANES (4, 8 or 16) lanes; every lane of a group
+// receives the group's sum.  quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+// row_half_mirror, row_mirror.
+template <int LANES>
+__device__ __forceinline__ float group_sum(float x) {
+  x += dpp_f<0xB1>(x);
+  x += dpp_f<0x4E>(x);
+  if constexpr (LANES >= 8) x += dpp_f<0x141>(x);
+  if constexpr (LANES >= 16) x += dpp_f<0x140>(x);
+  return x;
+}
+
+// Zero the bf16 elements of an 8-token chunk starting at `first` whose token
+// index is >= `valid` (slots past the end of a sequence may hold anything).
+__device__ __forceinline__ u32x4 zero_tail(u32x4 v, int first, int valid) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int t = first + 2 * e;
+    uint32_t w = v[e];
+    if (t >= valid) w = 0u;
+    else if (t + 1 >= valid) w &= 0x0000ffffu;
+    v[e] = w;
+  }
+  return v;
+}
+
+// Destination of packed row r of an item: final (token, head) row or a
+// partial row of the workspace.
+__device__ __forceinline__ void store_result(const AttnArgs& a, const SeqRec& sq, const ItemRec& it,
+                                             int D, int r, int d0, const float* vals, int n,
+                                             bool write_lse, float lse_val) {
+  if (it.slot < 0) {
+    const int row = it.row0 + r;
+    const int j = row / a.group;
+    const int h = it.kv_head * a.group + row % a.group;
+    const size_t idx = size_t(sq.q_start + j) * a.hq + h;
+    if (a.out_bf16) {
+      __bf16* o = reinterpret_cast<__bf16*>(a.out) + idx * D + d0;
+      for (int e = 0; e < n; ++e) o[e] = __bf16(vals[e]);
+    } else {
+      float* o = reinterpret_cast<float*>(a.out) + idx * D + d0;
+      for (int e = 0; e < n; ++e) o[e] = vals[e];
+    }
+    if (write_lse && a.lse) a.lse[idx] = lse_val;
+  } else {
+    float* o = a.ws_o + size_t(it.slot + r) * D + d0;
+    for (int e = 0; e < n; ++e) o[e] = vals[e];
+    if (write_lse) a.ws_lse[it.slot + r] = lse_val;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Vector-ALU path: up to NR query rows of one (sequence, kv head) over the
+// item's KV range.  Wavefront w handles 32-token sub-tiles w, w+4, w+8, ...
+// with its own online-softmax state; the four states merge at the end.
+// LDS use: per-wave probability exchange, then the cross-wave merge buffers.
+template <int D, int B, int NR>
+__device__ void valu_item(const AttnArgs& a, const ItemRec& it, float* smem) {
+  constexpr int LPT = D / 8;                // lanes holding one 16-byte-chunked K row
+  constexpr int TPI = 64 / LPT;             // tokens per K load instruction
+  constexpr int UK = kValuSubTile / TPI;    // K loads per sub-tile
+  constexpr int UV = D / 16;                // V^T loads per sub-tile (16 dims each)
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const SeqRec sq = a.seqs[it.seq];
+  const int32_t* bt = a.bt + sq.bt_off;
+  const int G = a.group, g = it.kv_head;
+  const int kv_valid = sq.kv_len;
+  const int ktok = lane / LPT, kdc = lane % LPT;
+  const int vd = lane >> 2, vtc = lane & 3;
+
+  u32x4 q[NR];
+  int lim[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    if (r < it.nrows) {
+      const int row = it.row0 + r, j = row / G, h = g * G + row % G;
+      q[r] = ld16(a.q + (size_t(sq.q_start + j) * a.hq + h) * D + 8 * kdc);
+      lim[r] = sq.ctx + j;
+    } else {
+      q[r] = u32x4{0u, 0u, 0u, 0u};
+      lim[r] = -1;
+    }
+  }
+  float m[NR], l[NR], acc[NR][UV];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    m[r] = -INFINITY;
+    l[r] = 0.f;
+#pragma unroll
+    for (int i = 0; i < UV; ++i) acc[r][i] = 0.f;
+  }
+  float* pbuf = smem + wave * (NR * kValuSubTile);
+
+  for (int t0 = it.kv0 + wave * kValuSubTile; t0 < it.kv1; t0 += kWaves * kValuSubTile) {
+    u32x4 kr[UK], vr[UV];
+    int blk_u = 0;
+    if constexpr (B >= kValuSubTile) blk_u = bt[t0 / B];
+#pragma unroll
+    for (int i = 0; i < UK; ++i) {
+      const int tok = t0 + i * TPI + ktok;
+      kr[i] = u32x4{0u, 0u, 0u, 0u};
+      if (tok < kv_valid) {
+        const int blk = (B >= kValuSubTile) ? blk_u : bt[tok / B];
+        kr[i] = ld16(a.kpool + ((size_t(blk) * a.hkv + g) * B + tok % B) * D + 8 * kdc);
+      }
+    }
+    const int vt = t0 + 8 * vtc;
+#pragma unroll
+    for (int i = 0; i < UV; ++i) {
+      vr[i] = u32x4{0u, 0u, 0u, 0u};
+      if (vt < kv_valid) {
+        const int blk = (B >= kValuSubTile) ? blk_u : bt[vt / B];
+        vr[i] = ld16(a.vpool + ((size_t(blk) * a.hkv + g) * D + vd + 16 * i) * B + vt % B);
+      }
+    }
+    if (vt < kv_valid && vt + 8 > kv_valid) {
+#pragma unroll
+      for (int i = 0; i < UV; ++i) vr[i] = zero_tail(vr[i], vt, kv_valid);
+    }
+
+    // scores (log2 units), masked by range and causal limit
+    float s[NR][UK];
+#pragma unroll
+    for (int i = 0; i < UK; ++i) {
+      const int tok = t0 + i * TPI + ktok;
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        float p = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p = dot2(q[r][e], kr[i][e], p);
+        p = group_sum<LPT>(p);
+        s[r][i] = (tok < it.kv1 && tok <= lim[r]) ? p * a.scale_log2 : -INFINITY;
+      }
+    }
+
+    float alpha[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      float mt = s[r][0];
+#pragma unroll
+      for (int i = 1; i < UK; ++i) mt = fmaxf(mt, s[r][i]);
+#pragma unroll
+      for (int x = LPT; x < 64; x <<= 1) mt = fmaxf(mt, __shfl_xor(mt, x));
+      const float mn = fmaxf(m[r], mt);
+      const float mref = (mn == -INFINITY) ? 0.f : mn;
+      alpha[r] = fast_exp2(m[r] - mref);
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < UK; ++i) {
+        s[r][i] = fast_exp2(s[r][i] - mref);
+        ps += s[r][i];
+      }
+      l[r] = l[r] * alpha[r] + ps;
+      m[r] = mn;
+    }
+
+    // probabilities: token-per-lane-group layout -> 8-token chunk per lane
+    if (kdc == 0) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int i = 0; i < UK; ++i) pbuf[r * kValuSubTile + i * TPI + ktok] = s[r][i];
+    }
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    float pp[NR][8];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(pbuf + r * kValuSubTile + 8 * vtc);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(pbuf + r * kValuSubTile + 8 * vtc + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pp[r][e] = x0[e];
+        pp[r][4 + e] = x1[e];
+      }
+    }
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+
+#pragma unroll
+    for (int i = 0; i < UV; ++i) {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] = bf_lo(vr[i][e]);
+        v[2 * e + 1] = bf_hi(vr[i][e]);
+      }
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        float t = acc[r][i] * alpha[r];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) t = fmaf(pp[r][u], v[u], t);
+        acc[r][i] = t;
+      }
+    }
+  }
+
+  // wavefront totals: l over token groups, acc over the 4 chunk lanes
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+#pragma unroll
+    for (int x = LPT; x < 64; x <<= 1) l[r] += __shfl_xor(l[r], x);
+#pragma unroll
+    for (int i = 0; i < UV; ++i) {
+      float t = acc[r][i];
+      t += dpp_f<0xB1>(t);
+      t += dpp_f<0x4E>(t);
+      acc[r][i] = t;
+    }
+  }
+
+  // cross-wavefront log-sum-exp merge
+  float* ms = smem + kWaves * NR * kValuSubTile;
+  float* ls = ms + kWaves * NR;
+  float* as = ls + kWaves * NR;
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      ms[wave * NR + r] = m[r];
+      ls[wave * NR + r] = l[r];
+    }
+  }
+  if (vtc == 0) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int i = 0; i < UV; ++i) as[(wave * NR + r) * D + vd + 16 * i] = acc[r][i];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < NR * D; idx += kThreads) {
+    const int r = idx / D, d = idx % D;
+    if (r >= it.nrows) continue;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, ms[w * NR + r]);
+    float o = 0.f, lse_val = -INFINITY;
+    if (mx != -INFINITY) {
+      float wsum = 0.f, os = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float f = fast_exp2(ms[w * NR + r] - mx);
+        wsum += ls[w * NR + r] * f;
+        os += as[(w * NR + r) * D + d] * f;
+      }
+      o = os / wsum;
+      lse_val = (mx + fast_log2(wsum)) * kLn2;
+    }
+    store_result(a, sq, it, D, r, d, &o, 1, d == 0, lse_val);
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Matrix-core path: up to 128 packed query rows (32 per wavefront, one per lane
+// pair l, l^32) of one (sequence, kv head) over the item's KV range, in
+// 64-token stages double-buffered through LDS.
+//
+// Stage layout in LDS (bf16): K rows [64][D+8] with the 32 tokens of each half
+// stored at row perm32(t) (bits 2 and 3 swapped), then V^T rows [D][64+8].
+// The padding keeps the 16-byte MFMA operand reads free of bank conflicts.
+//
+// With A = K rows and B = Q^T, lane l of the S^T product holds query row l%32
+// and the 16 tokens 16*(v>>3) + 8*(l/32) + (v&7), v = 0..15, of each 32-token
+// half; those are exactly the P^T operand of O^T = V^T P^T for the two 16-token
+// k-steps (elements 8*ks .. 8*ks+7), and the matching V^T operand is 8
+// contiguous tokens of one dimension.
+__device__ __forceinline__ int perm32(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
+
+template <int D>
+struct MfmaLds {
+  static constexpr int KS = D + 8;
+  static constexpr int VS = kKvTile + 8;
+  static constexpr int KT = kKvTile * KS;
+  static constexpr int VT = D * VS;
+  static constexpr int STAGE = KT + VT;
+  static constexpr int BYTES = 2 * STAGE * 2;
+};
+
+template <int D, int B>
+__device__ void mfma_item(const AttnArgs& a, const ItemRec& it, uint16_t* lds) {
+  using L = MfmaLds<D>;
+  constexpr int CPR = D / 8;                          // 16-byte chunks per K row
+  constexpr int KCH = kKvTile * CPR / kThreads;       // K chunks per thread per stage
+  constexpr int VCH = D * (kKvTile / 8) / kThreads;   // V^T chunks per thread per stage
+  static_assert(KCH * kThreads == kKvTile * CPR && VCH * kThreads == D * kKvTile / 8, "stage split");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const SeqRec sq = a.seqs[it.seq];
+  const int32_t* bt = a.bt + sq.bt_off;
+  const int G = a.group, g = it.kv_head, kv_valid = sq.kv_len;
+  const int r = wave * kMfmaRowsPerWave + l32;
+  const bool row_ok = r < it.nrows;
+  const int row = it.row0 + r;
+  const int j = row / G, h = g * G + row % G;
+  const int lim = row_ok ? sq.ctx + j : -1;
+  const bool active = wave < it.waves;
+
+  bf16x8 qb[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    if (row_ok) v = ld16(a.q + (size_t(sq.q_start + j) * a.hq + h) * D + 16 * kk + 8 * hf);
+    qb[kk] = __builtin_bit_cast(bf16x8, v);
+  }
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int dd = 0; dd < D / 32; ++dd)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) o[dd][v] = 0.f;
+  float m = -INFINITY, lsum = 0.f;
+
+  const int ntiles = (it.kv1 - it.kv0 + kKvTile - 1) / kKvTile;
+  const size_t kv_head_base = size_t(g);
+  u32x4 kst[KCH], vst[VCH];
+
+  auto load_stage = [&](int tb) {
+    int blk_u = 0;
+    if constexpr (B >= kKvTile) blk_u = bt[tb / B];
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) {
+      const int ch = tid + kThreads * c;
+      const int tok = ch / CPR, dc = ch % CPR, p = tb + tok;
+      kst[c] = u32x4{0u, 0u, 0u, 0u};
+      if (p < kv_valid) {
+        const int blk = (B >= kKvTile) ? blk_u : bt[p / B];
+        kst[c] = ld16(a.kpool + ((size_t(blk) * a.hkv + kv_head_base) * B + p % B) * D + 8 * dc);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < VCH; ++c) {
+      const int ch = tid + kThreads * c;
+      const int d = ch / (kKvTile / 8), tc = ch % (kKvTile / 8), p = tb + 8 * tc;
+      vst[c] = u32x4{0u, 0u, 0u, 0u};
+      if (p < kv_valid) {
+        const int blk = (B >= kKvTile) ? blk_u : bt[p / B];
+        vst[c] = ld16(a.vpool + ((size_t(blk) * a.hkv + kv_head_base) * D + d) * B + p % B);
+        if (p + 8 > kv_valid) vst[c] = zero_tail(vst[c], p, kv_valid);
+      }
+    }
+  };
+  auto store_stage = [&](int buf) {
+    uint16_t* kt = lds + buf * L::STAGE;
+    uint16_t* vt = kt + L::KT;
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) {
+      const int ch = tid + kThreads * c;
+      const int tok = ch / CPR, dc = ch % CPR;
+      const int prow = (tok & ~31) | perm32(tok & 31);
+      st16(kt + prow * L::KS + 8 * dc, kst[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < VCH; ++c) {
+      const int ch = tid + kThreads * c;
+      const int d = ch / (kKvTile / 8), tc = ch % (kKvTile / 8);
+      st16(vt + d * L::VS + 8 * tc, vst[c]);
+    }
+  };
+
+  load_stage(it.kv0);
+  store_stage(0);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int tb = it.kv0 + t * kKvTile;
+    if (t + 1 < ntiles) load_stage(tb + kKvTile);
+    if (active) {
+      const uint16_t* kt = lds + (t & 1) * L::STAGE;
+      const uint16_t* vt = kt + L::KT;
+      f32x16 sacc[2];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sacc[h2][v] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+          const bf16x8 ka = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4*>(kt + (32 * h2 + l32) * L::KS + 16 * kk + 8 * hf));
+          sacc[h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[kk], sacc[h2], 0, 0, 0);
+        }
+      }
+      float mt = -INFINITY;
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int tok = tb + 32 * h2 + 16 * (v >> 3) + 8 * hf + (v & 7);
+          const float x = (tok < it.kv1 && tok <= lim) ? sacc[h2][v] * a.scale_log2 : -INFINITY;
+          sacc[h2][v] = x;
+          mt = fmaxf(mt, x);
+        }
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const float mn = fmaxf(m, mt);
+      const float mref = (mn == -INFINITY) ? 0.f : mn;
+      const float alpha = fast_exp2(m - mref);
+      float ps = 0.f;
+      bf16x8 pb[2][2];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float p = fast_exp2(sacc[h2][v] - mref);
+          ps += p;
+          pb[h2][v >> 3][v & 7] = __bf16(p);
+        }
+      lsum = lsum * alpha + ps;
+      m = mn;
+#pragma unroll
+      for (int dd = 0; dd < D / 32; ++dd) o[dd] *= alpha;
+#pragma unroll
+      for (int dd = 0; dd < D / 32; ++dd)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const bf16x8 va = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4*>(vt + (32 * dd + l32) * L::VS + 32 * h2 + 16 * ks + 8 * hf));
+            o[dd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[h2][ks], o[dd], 0, 0, 0);
+          }
+    }
+    if (t + 1 < ntiles) store_stage((t + 1) & 1);
+    __syncthreads();
+  }
+
+  if (active) {
+    const float lt = lsum + __shfl_xor(lsum, 32);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float lse_val = lt > 0.f ? (m + fast_log2(lt)) * kLn2 : -INFINITY;
+    if (row_ok) {
+#pragma unroll
+      for (int dd = 0; dd < D / 32; ++dd)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          float vals[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vals[e] = o[dd][4 * qd + e] * inv;
+          store_result(a, sq, it, D, r, 32 * dd + 8 * qd + 4 * hf, vals, 4,
+                       hf == 0 && dd == 0 && qd == 0, lse_val);
+        }
+    }
+  }
+}
+
+template <int D>
+constexpr int valu_lds_bytes() {
+  return (kWaves * kValuMaxRows * kValuSubTile + 2 * kWaves * kValuMaxRows +
+          kWaves * kValuMaxRows * D) * 4;
+}
+
+template <int D, int B, bool MFMA>
+__global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
+  constexpr int kLds = MFMA ? (MfmaLds<D>::BYTES > valu_lds_bytes<D>() ? MfmaLds<D>::BYTES
+                                                                        : valu_lds_bytes<D>())
+                            : valu_lds_bytes<D>();
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kLds];
+  const ItemRec it = a.items[blockIdx.x];
+  if constexpr (MFMA) {
+    if (int(blockIdx.x) < a.n_mfma) {
+      mfma_item<D, B>(a, it, reinterpret_cast<uint16_t*>(smem));
+      return;
+    }
+  }
+  if (it.nrows == 1)
+    valu_item<D, B, 1>(a, it, reinterpret_cast<float*>(smem));
+  else
+    valu_item<D, B, kValuMaxRows>(a, it, reinterpret_cast<float*>(smem));
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void merge_kernel(AttnArgs a, const MergeRec* merges) {
+  const MergeRec mg = merges[blockIdx.x];
+  const SeqRec sq = a.seqs[mg.seq];
+  ItemRec it;
+  it.seq = mg.seq;
+  it.kv_head = mg.kv_head;
+  it.row0 = mg.row0;
+  it.nrows = mg.nrows;
+  it.slot = -1;
+  for (int idx = threadIdx.x; idx < mg.nrows * D; idx += kThreads) {
+    const int r = idx / D, d = idx % D;
+    float mx = -INFINITY;
+    for (int i = 0; i < mg.nsplit; ++i) mx = fmaxf(mx, a.ws_lse[mg.slot0 + i * mg.nrows + r]);
+    float wsum = 0.f, os = 0.f;
+    for (int i = 0; i < mg.nsplit; ++i) {
+      const int pr = mg.slot0 + i * mg.nrows + r;
+      const float li = a.ws_lse[pr];
+      const float w = (li == -INFINITY) ? 0.f : fast_exp2((li - mx) * kLog2e);
+      wsum += w;
+      os += w * a.ws_o[size_t(pr) * D + d];
+    }
+    const float o = os / wsum;
+    const float lse_val = mx + fast_log2(wsum) * kLn2;
+    store_result(a, sq, it, D, r, d, &o, 1, d == 0, lse_val);
+  }
+}
+
+template <int D, int B>
+__global__ __launch_bounds__(kThreads) void append_kernel(const RunRec* runs, const uint16_t* k_new,
+                                                           const uint16_t* v_new, uint16_t* kpool,
+                                                           uint16_t* vpool, int hkv) {
+  constexpr int CPR = D / 8;
+  constexpr int VS = D + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t vtile[B * VS];
+  const RunRec run = runs[blockIdx.x];
+  const int g = blockIdx.y;
+  uint16_t* kdst = kpool + ((size_t(run.block) * hkv + g) * B + run.slot0) * D;
+  for (int c = threadIdx.x; c < run.count * CPR; c += kThreads) {
+    const int i = c / CPR, dc = c % CPR;
+    const size_t src = (size_t(run.tok0 + i) * hkv + g) * D + 8 * dc;
+    st16(kdst + i * D + 8 * dc, ld16(k_new + src));
+    st16(vtile + i * VS + 8 * dc, ld16(v_new + src));
+  }
+  __syncthreads();
+  uint16_t* vdst = vpool + (size_t(run.block) * hkv + g) * D * B + run.slot0;
+  for (int e = threadIdx.x; e < run.count * D; e += kThreads) {
+    const int d = e / run.count, i = e % run.count;
+    vdst[size_t(d) * B + i] = vtile[i * VS + d];
+  }
+}
+
+// ---------------------------------------------------------------- profiling
+struct ProfRec {
+  int kind;
+  hipEvent_t start, stop;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof_recs;
+std::vector<hipEvent_t> g_prof_pool;
+
+hipEvent_t prof_event() {
+  if (!g_prof_pool.empty()) {
+    hipEvent_t e = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+struct ProfScope {
+  int kind;
+  hipStream_t stream;
+  hipEvent_t start = nullptr;
+  ProfScope(int k, hipStream_t s) : kind(k), stream(s) {
+    if (!g_prof_on) return;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    start = prof_event();
+    if (start) hipEventRecord(start, stream);
+  }
+  ~ProfScope() {
+    if (!start) return;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    hipEvent_t stop = prof_event();
+    if (!stop) return;
+    hipEventRecord(stop, stream);
+    g_prof_recs.push_back({kind, start, stop});
+  }
+};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define FG_SWITCH_DB(D_, B_, MACRO)                 \
+  do {                                              \
+    if ((D_) == 64 && (B_) == 16) MACRO(64, 16);    \
+    else if ((D_) == 64 && (B_) == 32) MACRO(64, 32); \
+    else if ((D_) == 64 && (B_) == 64) MACRO(64, 64); \
+    else if ((D_) == 128 && (B_) == 16) MACRO(128, 16); \
+    else if ((D_) == 128 && (B_) == 32) MACRO(128, 32); \
+    else if ((D_) == 128 && (B_) == 64) MACRO(128, 64); \
+    else return FG_E_UNSUPPORTED;                   \
+  } while (0)
+
+}  // namespace
+}  // namespace fg
+
+using namespace fg;
+
+extern "C" int fg_internal_device_cu_count(void) {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  return n;
+}
+
+extern "C" fg_status fg_plan_upload(const fg_plan* plan, void* d_meta, void* stream) {
+  if (!plan || !d_meta || !aligned16(d_meta)) return FG_E_INVALID;
+  if (hipMemcpyAsync(d_meta, plan->blob.data(), plan->blob.size(), hipMemcpyHostToDevice,
+                     static_cast<hipStream_t>(stream)) != hipSuccess)
+    return FG_E_HIP;
+  return FG_OK;
+}
+
+extern "C" fg_status fg_kv_append(const fg_plan* plan, const void* d_meta, const void* k_new,
+                                  const void* v_new, void* k_pool, void* v_pool, void* stream) {
+  if (!plan) return FG_E_INVALID;
+  if (plan->n_runs == 0) return FG_OK;
+  if (!d_meta || !k_new || !v_new || !k_pool || !v_pool) return FG_E_INVALID;
+  if (!aligned16(d_meta) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) ||
+      !aligned16(v_pool))
+    return FG_E_INVALID;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const RunRec* runs =
+      reinterpret_cast<const RunRec*>(static_cast<const uint8_t*>(d_meta) + plan->off_runs);
+  ProfScope prof(FG_KERNEL_APPEND, s);
+  const dim3 grid(unsigned(plan->n_runs), unsigned(plan->hkv));
+#define FG_LAUNCH_APPEND(D_, B_)                                                              \
+  hipLaunchKernelGGL((append_kernel<D_, B_>), grid, dim3(kThreads), 0, s, runs,              \
+                     static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), \
+                     static_cast<uint16_t*>(k_pool), static_cast<uint16_t*>(v_pool), plan->hkv)
+  FG_SWITCH_DB(plan->head_dim, plan->block_size, FG_LAUNCH_APPEND);
+#undef FG_LAUNCH_APPEND
+  return hipGetLastError() == hipSuccess ? FG_OK : FG_E_HIP;
+}
+
+extern "C" fg_status fg_attention_ragged(const fg_plan* plan, const void* d_meta, const void* q,
+                                         const void* k_pool, const void* v_pool, void* out,
+                                         int32_t out_dtype, float* lse, void* d_ws,
+                                         size_t ws_bytes, void* stream) {
+  if (!plan) return FG_E_INVALID;
+  if (out_dtype != FG_DTYPE_F32 && out_dtype != FG_DTYPE_BF16) return FG_E_UNSUPPORTED;
+  if (plan->n_items == 0) return FG_OK;
+  if (!d_meta || !q || !k_pool || !v_pool || !out) return FG_E_INVALID;
+  if (!aligned16(d_meta) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) ||
+      !aligned16(out) || (lse && !aligned16(lse)))
+    return FG_E_INVALID;
+  if (plan->ws_bytes > 0 && (!d_ws || ws_bytes < plan->ws_bytes || !aligned16(d_ws)))
+    return FG_E_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint8_t* meta = static_cast<const uint8_t*>(d_meta);
+  AttnArgs a;
+  a.seqs = reinterpret_cast<const SeqRec*>(meta + plan->off_seqs);
+  a.bt = reinterpret_cast<const int32_t*>(meta + plan->off_bt);
+  a.items = reinterpret_cast<const ItemRec*>(meta + plan->off_items);
+  a.q = static_cast<const uint16_t*>(q);
+  a.kpool = static_cast<const uint16_t*>(k_pool);
+  a.vpool = static_cast<const uint16_t*>(v_pool);
+  a.out = out;
+  a.lse = lse;
+  a.ws_o = plan->ws_bytes ? reinterpret_cast<float*>(static_cast<uint8_t*>(d_ws) + plan->ws_o_off) : nullptr;
+  a.ws_lse = plan->ws_bytes ? reinterpret_cast<float*>(static_cast<uint8_t*>(d_ws) + plan->ws_lse_off) : nullptr;
+  a.hq = plan->hq;
+  a.hkv = plan->hkv;
+  a.group = plan->group;
+  a.n_mfma = plan->n_mfma;
+  a.scale_log2 = plan->scale * kLog2e;
+  a.out_bf16 = out_dtype == FG_DTYPE_BF16;
+
+  {
+    ProfScope prof(FG_KERNEL_ATTENTION, s);
+    const dim3 grid(unsigned(plan->n_items));
+#define FG_LAUNCH_ATTN(D_, B_)                                                                 \
+  do {                                                                                         \
+    if (plan->n_mfma > 0)                                                                      \
+      hipLaunchKernelGGL((attn_kernel<D_, B_, true>), grid, dim3(kThreads), 0, s, a);          \
+    else                                                                                       \
+      hipLaunchKernelGGL((attn_kernel<D_, B_, false>), grid, dim3(kThreads), 0, s, a);         \
+  } while (0)
+    FG_SWITCH_DB(plan->head_dim, plan->block_size, FG_LAUNCH_ATTN);
+#undef FG_LAUNCH_ATTN
+    if (hipGetLastError() != hipSuccess) return FG_E_HIP;
+  }
+  if (plan->n_merge > 0) {
+    ProfScope prof(FG_KERNEL_MERGE, s);
+    const MergeRec* merges = reinterpret_cast<const MergeRec*>(meta + plan->off_merges);
+    const dim3 grid(unsigned(plan->n_merge));
+    if (plan->head_dim == 64)
+      hipLaunchKernelGGL((merge_kernel<64>), grid, dim3(kThreads), 0, s, a, merges);
+    else
+      hipLaunchKernelGGL((merge_kernel<128>), grid, dim3(kThreads), 0, s, a, merges);
+    if (hipGetLastError() != hipSuccess) return FG_E_HIP;
+  }
+  return FG_OK;
+}
+
+extern "C" fg_status fg_profile_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = on != 0;
+  return FG_OK;
+}
+
+extern "C" fg_status fg_profile_read(double* total_ms, int32_t* launches, int32_t n_kernels) {
+  if (n_kernels < 0 || (n_kernels > 0 && (!total_ms || !launches))) return FG_E_INVALID;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (int i = 0; i < n_kernels; ++i) {
+    total_ms[i] = 0.0;
+    launches[i] = 0;
+  }
+  fg_status st = FG_OK;
+  for (const ProfRec& r : g_prof_recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.stop) != hipSuccess ||
+        hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess)
+      st = FG_E_HIP;
+    if (r.kind < n_kernels) {
+      total_ms[r.kind] += ms;
+      launches[r.kind] += 1;
+    }
+    g_prof_pool.push_back(r.start);
+    g_prof_pool.push_back(r.stop);
+  }
+  g_prof_recs.clear();
+  return st;
+}
+
+extern "C" const char* fg_kernel_name(int32_t id) {
+  switch (id) {
+    case FG_KERNEL_APPEND: return "append_kernel";
+    case FG_KERNEL_ATTENTION: return "attn_kernel";
+    case FG_KERNEL_MERGE: return "merge_kernel";
+    default: return "unknown";
+  }
+}

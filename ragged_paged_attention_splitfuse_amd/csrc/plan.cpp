@@ -1,0 +1,341 @@
+// plan.cpp -- host planner of one ragged paged attention pass.
+//
+// Validates the pass description, packs per-sequence records and the used
+// block-table entries, cuts the new tokens into per-block append runs, and
+// builds the attention work list: query rows of each (sequence, kv head) are
+// grouped (few rows -> vector-ALU items, many rows -> 128-row matrix-core
+// tiles), and each group's visible KV range is split over compute units when
+// it is long compared with the pass's total work.  Split partials are merged
+// by log-sum-exp afterwards.
+//
+// The length-aware split follows the adaptive split-KV idea of "DeepSpeed-
+// FastGen Guide: Dynamic SplitKV Serving" (section "1. Dynamic SplitKV
+// Attention": split counts follow each request's length and the number of
+// compute units; short requests are not split).  The policy itself is ours:
+// a cost model in KV tokens, a per-item target derived from the total work
+// and the CU count, splits aligned to the 64-token KV stage, and
+// longest-first ordering of the work items.
+#include "plan.h"
+
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+#include <numeric>
+
+namespace {
+
+using fg::ItemRec;
+using fg::MergeRec;
+using fg::RunRec;
+using fg::SeqRec;
+
+constexpr int64_t kMaxTokens = int64_t(1) << 28;
+constexpr int64_t kMaxKvLen = int64_t(1) << 28;
+constexpr int kDefaultMinSplitTokens = 256;
+constexpr int kDefaultMaxSplits = 64;
+constexpr int kMaxSplitsLimit = 256;
+// Concurrent work-groups per CU assumed by the balance target, and how many
+// items each such slot should receive at least.
+constexpr int kSlotsPerCu = 2;
+constexpr int kItemsPerSlot = 4;
+
+size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Group {
+  int32_t seq, kv_head, row0, nrows, vis_end, waves;  // waves 0: vector-ALU path
+  double cost;
+};
+
+struct Pending {
+  ItemRec item;
+  double cost;
+  int32_t order;
+};
+
+fg_status validate(const fg_pass_desc* d) {
+  if (d->num_seqs < 0) return FG_E_INVALID;
+  if (d->num_q_heads < 1 || d->num_kv_heads < 1) return FG_E_INVALID;
+  if (d->num_q_heads % d->num_kv_heads != 0) return FG_E_INVALID;
+  if (d->head_dim != 64 && d->head_dim != 128) return FG_E_UNSUPPORTED;
+  if (d->block_size != 16 && d->block_size != 32 && d->block_size != 64) return FG_E_UNSUPPORTED;
+  if (d->num_blocks < 1 || d->max_blocks_per_seq < 0) return FG_E_INVALID;
+  if (!isfinite(d->scale) || d->scale < 0.f) return FG_E_INVALID;
+  if (d->target_cus < 0 || d->min_split_tokens < 0) return FG_E_INVALID;
+  if (d->max_splits < 0 || d->max_splits > kMaxSplitsLimit) return FG_E_INVALID;
+  if (d->force_splits < 0 || d->force_splits > kMaxSplitsLimit) return FG_E_INVALID;
+  if (d->num_seqs > 0 && (!d->q_lens || !d->ctx_lens || !d->block_tables)) return FG_E_INVALID;
+  return FG_OK;
+}
+
+}  // namespace
+
+extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
+  if (!d || !out_plan) return FG_E_INVALID;
+  *out_plan = nullptr;
+  fg_status st = validate(d);
+  if (st != FG_OK) return st;
+
+  try {
+    const int S = d->num_seqs;
+    const int B = d->block_size;
+    const int D = d->head_dim;
+    const int G = d->num_q_heads / d->num_kv_heads;
+    const int MB = d->max_blocks_per_seq;
+
+    // ---- per-sequence records and block-table validation
+    std::vector<SeqRec> seqs(S);
+    int64_t tokens = 0, used_blocks = 0;
+    for (int s = 0; s < S; ++s) {
+      const int64_t q = d->q_lens[s], c = d->ctx_lens[s];
+      if (q < 1 || c < 0) return FG_E_RANGE;
+      const int64_t kv = q + c;
+      if (kv > kMaxKvLen) return FG_E_RANGE;
+      const int64_t nblk = ceil_div(kv, B);
+      if (nblk > MB) return FG_E_RANGE;
+      SeqRec& r = seqs[s];
+      r.q_start = int32_t(tokens);
+      r.q_len = int32_t(q);
+      r.ctx = int32_t(c);
+      r.kv_len = int32_t(kv);
+      r.bt_off = int32_t(used_blocks);
+      r.nblk = int32_t(nblk);
+      r.pad0 = r.pad1 = 0;
+      tokens += q;
+      used_blocks += nblk;
+      if (tokens > kMaxTokens) return FG_E_RANGE;
+    }
+    std::vector<int32_t> bt(static_cast<size_t>(used_blocks));
+    std::vector<uint8_t> seen(size_t(d->num_blocks), 0);
+    for (int s = 0; s < S; ++s) {
+      const int32_t* row = d->block_tables + int64_t(s) * MB;
+      for (int b = 0; b < seqs[s].nblk; ++b) {
+        const int32_t id = row[b];
+        if (id < 0 || id >= d->num_blocks) return FG_E_RANGE;
+        if (seen[id]) return FG_E_ALIAS;
+        seen[id] = 1;
+        bt[size_t(seqs[s].bt_off) + b] = id;
+      }
+    }
+
+    int target_cus = d->target_cus;
+    if (target_cus == 0) {
+      target_cus = fg_internal_device_cu_count();
+      if (target_cus < 1) return FG_E_HIP;
+    }
+    const int min_split = d->min_split_tokens ? d->min_split_tokens : kDefaultMinSplitTokens;
+    const int max_splits = d->max_splits ? d->max_splits : kDefaultMaxSplits;
+
+    // ---- append runs: consecutive new tokens of a sequence within one block
+    std::vector<RunRec> runs;
+    for (int s = 0; s < S; ++s) {
+      const SeqRec& r = seqs[s];
+      int64_t p = r.ctx;
+      while (p < r.kv_len) {
+        const int64_t bi = p / B;
+        const int64_t end = std::min<int64_t>(r.kv_len, (bi + 1) * B);
+        RunRec run;
+        run.tok0 = int32_t(r.q_start + (p - r.ctx));
+        run.slot0 = int32_t(p % B);
+        run.count = int32_t(end - p);
+        run.block = bt[size_t(r.bt_off + bi)];
+        runs.push_back(run);
+        p = end;
+      }
+    }
+
+    // ---- row groups and their costs (KV tokens visible to the group: a
+    // decode group streams them from HBM, a full 128-row tile spends about the
+    // same time on matrix-core work per token at the MI355X flop:byte ratio)
+    std::vector<Group> groups;
+    double total_cost = 0.0;
+    for (int s = 0; s < S; ++s) {
+      const SeqRec& r = seqs[s];
+      const int rows = r.q_len * G;
+      for (int g = 0; g < d->num_kv_heads; ++g) {
+        if (rows <= fg::kValuMaxRows) {
+          Group grp{s, g, 0, rows, r.kv_len, 0, double(r.kv_len)};
+          groups.push_back(grp);
+          total_cost += grp.cost;
+        } else {
+          for (int r0 = 0; r0 < rows; r0 += fg::kMfmaTileRows) {
+            const int nr = std::min(fg::kMfmaTileRows, rows - r0);
+            const int j_last = (r0 + nr - 1) / G;
+            const int vis = r.ctx + j_last + 1;
+            const int waves = (nr + fg::kMfmaRowsPerWave - 1) / fg::kMfmaRowsPerWave;
+            Group grp{s, g, r0, nr, vis, waves, double(vis)};
+            groups.push_back(grp);
+            total_cost += grp.cost;
+          }
+        }
+      }
+    }
+
+    // ---- split each group's visible range [0, vis_end)
+    const double target =
+        std::max(1.0, total_cost / double(int64_t(target_cus) * kSlotsPerCu * kItemsPerSlot));
+    std::vector<Pending> mfma, valu;
+    std::vector<MergeRec> merges;
+    int64_t partial_rows = 0;
+    int max_used = 1;
+    int32_t order = 0;
+    for (const Group& grp : groups) {
+      int64_t k;
+      if (d->force_splits > 0) {
+        k = d->force_splits;
+      } else {
+        k = int64_t(ceil(grp.cost / target));
+        k = std::min<int64_t>(k, max_splits);
+        k = std::min<int64_t>(k, std::max<int64_t>(1, grp.vis_end / std::max(1, min_split)));
+      }
+      k = std::max<int64_t>(1, std::min<int64_t>(k, ceil_div(grp.vis_end, fg::kKvTile)));
+      const int64_t chunk = ceil_div(ceil_div(grp.vis_end, k), fg::kKvTile) * fg::kKvTile;
+      k = ceil_div(grp.vis_end, chunk);
+      max_used = std::max<int>(max_used, int(k));
+      int32_t slot0 = -1;
+      if (k > 1) {
+        if (partial_rows + k * grp.nrows > INT32_MAX) return FG_E_RANGE;
+        slot0 = int32_t(partial_rows);
+        partial_rows += k * grp.nrows;
+        MergeRec m;
+        m.seq = grp.seq;
+        m.kv_head = grp.kv_head;
+        m.row0 = grp.row0;
+        m.nrows = grp.nrows;
+        m.nsplit = int32_t(k);
+        m.slot0 = slot0;
+        m.pad0 = m.pad1 = 0;
+        merges.push_back(m);
+      }
+      for (int64_t i = 0; i < k; ++i) {
+        Pending p;
+        p.item.seq = grp.seq;
+        p.item.kv_head = grp.kv_head;
+        p.item.row0 = grp.row0;
+        p.item.nrows = grp.nrows;
+        p.item.kv0 = int32_t(i * chunk);
+        p.item.kv1 = int32_t(std::min<int64_t>(grp.vis_end, (i + 1) * chunk));
+        p.item.slot = k > 1 ? int32_t(slot0 + i * grp.nrows) : -1;
+        p.item.waves = grp.waves;
+        p.cost = double(p.item.kv1 - p.item.kv0) * (grp.cost / double(grp.vis_end));
+        p.order = order++;
+        (grp.waves ? mfma : valu).push_back(p);
+      }
+    }
+
+    // Longest first within each path (ties keep plan order: deterministic).
+    auto longest_first = [](const Pending& a, const Pending& b) {
+      if (a.cost != b.cost) return a.cost > b.cost;
+      return a.order < b.order;
+    };
+    std::sort(mfma.begin(), mfma.end(), longest_first);
+    std::sort(valu.begin(), valu.end(), longest_first);
+
+    // ---- pack the metadata blob
+    fg_plan* plan = new fg_plan();
+    plan->num_seqs = S;
+    plan->num_tokens = int32_t(tokens);
+    plan->hq = d->num_q_heads;
+    plan->hkv = d->num_kv_heads;
+    plan->group = G;
+    plan->head_dim = D;
+    plan->block_size = B;
+    plan->num_blocks = d->num_blocks;
+    plan->scale = d->scale > 0.f ? d->scale : float(1.0 / sqrt(double(D)));
+    plan->n_runs = int32_t(runs.size());
+    plan->n_mfma = int32_t(mfma.size());
+    plan->n_valu = int32_t(valu.size());
+    plan->n_items = plan->n_mfma + plan->n_valu;
+    plan->n_merge = int32_t(merges.size());
+    plan->n_partial_rows = int32_t(partial_rows);
+    plan->max_splits_used = max_used;
+    plan->target_cus = target_cus;
+
+    size_t off = 0;
+    plan->off_seqs = off;   off = align16(off + sizeof(SeqRec) * seqs.size());
+    plan->off_bt = off;     off = align16(off + sizeof(int32_t) * bt.size());
+    plan->off_runs = off;   off = align16(off + sizeof(RunRec) * runs.size());
+    plan->off_items = off;  off = align16(off + sizeof(ItemRec) * size_t(plan->n_items));
+    plan->off_merges = off; off = align16(off + sizeof(MergeRec) * merges.size());
+    plan->blob.assign(std::max<size_t>(off, 16), 0);
+    uint8_t* base = plan->blob.data();
+    if (!seqs.empty()) memcpy(base + plan->off_seqs, seqs.data(), sizeof(SeqRec) * seqs.size());
+    if (!bt.empty()) memcpy(base + plan->off_bt, bt.data(), sizeof(int32_t) * bt.size());
+    if (!runs.empty()) memcpy(base + plan->off_runs, runs.data(), sizeof(RunRec) * runs.size());
+    ItemRec* items = reinterpret_cast<ItemRec*>(base + plan->off_items);
+    for (size_t i = 0; i < mfma.size(); ++i) items[i] = mfma[i].item;
+    for (size_t i = 0; i < valu.size(); ++i) items[mfma.size() + i] = valu[i].item;
+    if (!merges.empty())
+      memcpy(base + plan->off_merges, merges.data(), sizeof(MergeRec) * merges.size());
+
+    plan->ws_o_off = 0;
+    plan->ws_lse_off = (size_t(partial_rows) * D * sizeof(float) + 255) & ~size_t(255);
+    plan->ws_bytes = partial_rows ? plan->ws_lse_off + size_t(partial_rows) * sizeof(float) : 0;
+    *out_plan = plan;
+    return FG_OK;
+  } catch (const std::bad_alloc&) {
+    return FG_E_NOMEM;
+  } catch (...) {
+    return FG_E_INVALID;
+  }
+}
+
+extern "C" fg_status fg_plan_info(const fg_plan* p, fg_plan_info_t* o) {
+  if (!p || !o) return FG_E_INVALID;
+  memset(o, 0, sizeof(*o));
+  o->num_tokens = p->num_tokens;
+  o->metadata_bytes = int64_t(p->blob.size());
+  o->workspace_bytes = int64_t(p->ws_bytes);
+  o->num_items = p->n_items;
+  o->num_valu_items = p->n_valu;
+  o->num_mfma_items = p->n_mfma;
+  o->num_merge_groups = p->n_merge;
+  o->num_partial_rows = p->n_partial_rows;
+  o->max_splits_used = p->max_splits_used;
+  o->num_append_runs = p->n_runs;
+  o->target_cus = p->target_cus;
+  return FG_OK;
+}
+
+extern "C" fg_status fg_plan_metadata(const fg_plan* p, void* host_dst, size_t bytes,
+                                      fg_plan_layout_t* layout) {
+  if (!p) return FG_E_INVALID;
+  if (host_dst) {
+    if (bytes < p->blob.size()) return FG_E_INVALID;
+    memcpy(host_dst, p->blob.data(), p->blob.size());
+  }
+  if (layout) {
+    memset(layout, 0, sizeof(*layout));
+    layout->seqs = int64_t(p->off_seqs);
+    layout->block_ids = int64_t(p->off_bt);
+    layout->runs = int64_t(p->off_runs);
+    layout->items = int64_t(p->off_items);
+    layout->merges = int64_t(p->off_merges);
+    layout->num_seqs = p->num_seqs;
+    layout->num_block_ids = int32_t((p->off_runs - p->off_bt) / sizeof(int32_t));
+    layout->num_runs = p->n_runs;
+    layout->num_items = p->n_items;
+    layout->num_merges = p->n_merge;
+  }
+  return FG_OK;
+}
+
+extern "C" void fg_plan_destroy(fg_plan* p) { delete p; }
+
+extern "C" const char* fg_status_string(fg_status s) {
+  switch (s) {
+    case FG_OK: return "ok";
+    case FG_E_INVALID: return "invalid argument";
+    case FG_E_RANGE: return "value out of range";
+    case FG_E_ALIAS: return "physical block used twice in one pass";
+    case FG_E_UNSUPPORTED: return "unsupported head_dim, block_size or dtype";
+    case FG_E_WORKSPACE: return "workspace too small or misaligned";
+    case FG_E_HIP: return "HIP runtime error";
+    case FG_E_NOMEM: return "host allocation failed";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int32_t fg_abi_version(void) { return FG_ABI_VERSION; }

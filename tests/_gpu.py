@@ -1,0 +1,107 @@
+"""GPU-side helpers for the parity tests: device pools, history fill, one pass.
+
+Everything here goes through the C-ABI binding; the oracle side is built in
+tests/_passes.py from the same generator tensors.
+"""
+import numpy as np
+import torch
+
+from oracle import attention as ora
+from ragged_paged_attention_splitfuse_amd import binding as fgb
+from ragged_paged_attention_splitfuse_amd import workloads as wl
+from tests._passes import oracle_pools
+
+PLAN_CUS = 256
+
+
+def to_dev(bits):
+    """uint16 bf16 bits (numpy) -> contiguous bf16 device tensor, same bits."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda").view(torch.bfloat16)
+
+
+def to_host_bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def gpu_pools(spec, poison=True):
+    kshape, vshape = fgb.pool_shapes(spec.num_blocks, spec.num_kv_heads, spec.block_size, spec.head_dim)
+    fill = wl.BF16_NAN if poison else 0
+    kp = torch.full(kshape, fill, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    vp = torch.full(vshape, fill, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    return kp, vp
+
+
+def fill_history(spec, tens, kp, vp):
+    """Append each sequence's cached tokens through fg_kv_append."""
+    hist = spec.history_pass()
+    if hist is None:
+        return
+    q, c, bt, _ = hist
+    plan = fgb.Plan(q, c, bt, spec.num_q_heads, spec.num_kv_heads, spec.head_dim,
+                    spec.block_size, spec.num_blocks, target_cus=PLAN_CUS)
+    meta = plan.upload()
+    fgb.kv_append(plan, meta, to_dev(tens.hist_k), to_dev(tens.hist_v), kp, vp)
+    torch.cuda.synchronize()
+    plan.close()
+
+
+def run_pass(spec, tens, kp, vp, out_dtype=torch.float32, dev_inputs=None, **knobs):
+    """Plan, upload, append and attend one pass; returns (out, lse, plan)."""
+    knobs.setdefault("target_cus", 0)
+    plan = fgb.Plan.from_spec(spec, **knobs)
+    meta = plan.upload()
+    if dev_inputs is None:
+        dev_inputs = (to_dev(tens.q), to_dev(tens.k_new), to_dev(tens.v_new))
+    q, kn, vn = dev_inputs
+    fgb.kv_append(plan, meta, kn, vn, kp, vp)
+    t, hq, d = spec.num_tokens, spec.num_q_heads, spec.head_dim
+    out = torch.full((t, hq, d), float("nan"), dtype=out_dtype, device="cuda")
+    lse = torch.full((t, hq), float("nan"), dtype=torch.float32, device="cuda")
+    fgb.attention_ragged(plan, meta, q, kp, vp, out, lse)
+    torch.cuda.synchronize()
+    return out, lse, plan
+
+
+def full_gpu_pass(spec, tens=None, poison=True, out_dtype=torch.float32, **knobs):
+    if tens is None:
+        tens = wl.make_tensors(spec)
+    kp, vp = gpu_pools(spec, poison)
+    fill_history(spec, tens, kp, vp)
+    out, lse, plan = run_pass(spec, tens, kp, vp, out_dtype=out_dtype, **knobs)
+    return tens, kp, vp, out, lse, plan
+
+
+def subset(spec, tens, seqs):
+    """The pass restricted to `seqs`, physical blocks relabelled 0..k-1.
+
+    Attention of a sequence depends only on its own rows and blocks, and the
+    oracle's results are bit-invariant under block relabelling, so this is the
+    oracle input for sampled checks of a large pass.  Returns (sub_spec,
+    sub_tensors, row_index) where row_index maps the sub-pass rows back to
+    rows of the full pass.
+    """
+    seqs = list(seqs)
+    cu = np.zeros(spec.num_seqs + 1, np.int64)
+    cu[1:] = np.cumsum(spec.q_lens)
+    hcu = np.zeros(spec.num_seqs + 1, np.int64)
+    hcu[1:] = np.cumsum(spec.ctx_lens)
+    q_lens, ctx_lens = spec.q_lens[seqs], spec.ctx_lens[seqs]
+    need = [-(-int(q + c) // spec.block_size) for q, c in zip(q_lens, ctx_lens)]
+    tables = np.full((len(seqs), max(need)), -1, np.int32)
+    nxt = 0
+    for i, k in enumerate(need):
+        tables[i, :k] = np.arange(nxt, nxt + k)
+        nxt += k
+    sub = wl.PassSpec(spec.name + "-sub", spec.num_q_heads, spec.num_kv_heads, spec.head_dim,
+                      spec.block_size, nxt, q_lens.copy(), ctx_lens.copy(), tables, spec.seed, spec.scale)
+    rows = np.concatenate([np.arange(cu[s], cu[s + 1]) for s in seqs])
+    hrows = np.concatenate([np.arange(hcu[s], hcu[s + 1]) for s in seqs])
+    st = wl.PassTensors(q=tens.q[rows], k_new=tens.k_new[rows], v_new=tens.v_new[rows],
+                        hist_k=tens.hist_k[hrows], hist_v=tens.hist_v[hrows])
+    return sub, st, rows
+
+
+def oracle_pass(spec, tens):
+    kp, vp = oracle_pools(spec, tens, poison=True)
+    return ora.attend(tens.q, kp, vp, spec.q_lens, spec.ctx_lens, spec.block_tables,
+                      spec.block_size, spec.num_kv_heads, scale=spec.scale or None)

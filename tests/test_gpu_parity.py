@@ -1,0 +1,203 @@
+"""GPU parity: the HIP path through the C ABI against the float64 CPU oracle.
+
+Bars: KV append and block addressing bit-exact; attention max-abs error
+<= 1e-2 on O (fp32 output; bf16 in, fp32 accumulate) and <= 1e-3 on LSE.
+Inputs are the seeded generator's; pools start poisoned with bf16 NaN so that
+any read of an unwritten slot shows up.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as ora
+from ragged_paged_attention_splitfuse_amd import binding as fgb
+from ragged_paged_attention_splitfuse_amd import workloads as wl
+from tests import _gpu as G
+from tests._passes import oracle_pools
+from tests._plan_check import check_plan
+
+pytestmark = pytest.mark.gpu
+
+O_TOL = 1e-2
+LSE_TOL = 1e-3
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def compare(o_gpu, lse_gpu, o_ref, lse_ref, what, rows=None):
+    o = o_gpu.float().cpu().numpy().astype(np.float64)
+    lg = lse_gpu.cpu().numpy().astype(np.float64)
+    if rows is not None:
+        o, lg = o[rows], lg[rows]
+    assert np.all(np.isfinite(o)), f"{what}: non-finite output"
+    eo = float(np.max(np.abs(o - o_ref))) if o.size else 0.0
+    el = float(np.max(np.abs(lg - lse_ref))) if lg.size else 0.0
+    _log(f"[parity] {what}: max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert eo <= O_TOL, f"{what}: O error {eo}"
+    assert el <= LSE_TOL, f"{what}: LSE error {el}"
+    return eo, el
+
+
+SMALL_SPECS = {
+    "tiny": lambda: wl.config_spec(1),
+    "mha_d128_b64_mixed": lambda: wl.custom_spec(
+        "a", [1, 300, 1, 2, 77, 1], [2500, 131, 0, 64, 1000, 63], 4, 4, 128, 64, seed=21),
+    "gqa8_d128_b64_mixed": lambda: wl.custom_spec(
+        "b", [1, 1, 130, 40, 1], [700, 2, 333, 0, 129], 16, 2, 128, 64, seed=22),
+    "mha_d64_b32_mixed": lambda: wl.custom_spec(
+        "c", [3, 1, 90, 4], [10, 1500, 45, 300], 6, 6, 64, 32, seed=23),
+    "gqa4_d64_b16_mixed": lambda: wl.custom_spec(
+        "d", [1, 50, 1, 2], [333, 17, 1, 900], 8, 2, 64, 16, seed=24),
+    "gqa2_d128_b16_mixed": lambda: wl.custom_spec(
+        "e", [2, 1, 65, 1], [100, 999, 300, 0], 4, 2, 128, 16, seed=25),
+    "gqa3_d128_b32_mixed": lambda: wl.custom_spec(
+        "f", [1, 41, 7], [450, 200, 60], 6, 2, 128, 32, seed=26),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL_SPECS))
+def test_attention_matches_oracle_small(name):
+    spec = SMALL_SPECS[name]()
+    _log(f"[case] small {name} S={spec.num_seqs} T={spec.num_tokens}")
+    tens, _, _, out, lse, plan = G.full_gpu_pass(spec)
+    check_plan(plan, spec)
+    o_ref, l_ref = G.oracle_pass(spec, tens)
+    compare(out, lse, o_ref, l_ref, name)
+
+
+@pytest.mark.parametrize("name", ["tiny", "mha_d128_b64_mixed", "gqa8_d128_b64_mixed", "gqa4_d64_b16_mixed"])
+def test_append_is_bit_exact(name):
+    spec = SMALL_SPECS[name]()
+    _log(f"[case] append {name}")
+    tens, kp, vp, _, _, _ = G.full_gpu_pass(spec)
+    kref, vref = oracle_pools(spec, tens, poison=True)
+    assert np.array_equal(G.to_host_bits(kp), kref)
+    assert np.array_equal(G.to_host_bits(vp), vref)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 7, 64])
+def test_forced_split_counts(k):
+    spec = SMALL_SPECS["mha_d128_b64_mixed"]()
+    _log(f"[case] forced splits k={k}")
+    tens, _, _, out, lse, plan = G.full_gpu_pass(spec, force_splits=k)
+    check_plan(plan, spec)
+    o_ref, l_ref = G.oracle_pass(spec, tens)
+    compare(out, lse, o_ref, l_ref, f"force_splits={k}")
+    _, _, _, out1, lse1, _ = G.full_gpu_pass(spec, tens=tens, force_splits=1)
+    assert float((out - out1).abs().max()) <= 1e-3
+    assert float((lse - lse1).abs().max()) <= 1e-3
+
+
+def test_forced_splits_gqa_tiles():
+    spec = SMALL_SPECS["gqa8_d128_b64_mixed"]()
+    tens, _, _, out, lse, plan = G.full_gpu_pass(spec, force_splits=5)
+    assert plan.info["num_merge_groups"] > 0
+    o_ref, l_ref = G.oracle_pass(spec, tens)
+    compare(out, lse, o_ref, l_ref, "gqa tiles force_splits=5")
+
+
+def test_block_permutation_is_bit_identical():
+    spec = SMALL_SPECS["gqa8_d128_b64_mixed"]()
+    tens, _, _, out, lse, _ = G.full_gpu_pass(spec)
+    perm = np.random.default_rng(5).permutation(spec.num_blocks).astype(np.int32)
+    spec2 = wl.PassSpec(**{**spec.__dict__})
+    spec2.block_tables = np.where(spec.block_tables >= 0, perm[spec.block_tables], -1).astype(np.int32)
+    _, _, _, out2, lse2, _ = G.full_gpu_pass(spec2, tens=tens)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+
+
+def test_repeat_runs_are_bit_identical():
+    spec = SMALL_SPECS["mha_d128_b64_mixed"]()
+    tens, kp, vp, out, lse, _ = G.full_gpu_pass(spec)
+    out2, lse2, _ = G.run_pass(spec, tens, kp, vp)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+
+
+def test_bf16_output_mode():
+    spec = SMALL_SPECS["gqa8_d128_b64_mixed"]()
+    tens, _, _, out, lse, _ = G.full_gpu_pass(spec, out_dtype=torch.bfloat16)
+    o_ref, l_ref = G.oracle_pass(spec, tens)
+    o = out.float().cpu().numpy().astype(np.float64)
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(o_ref), 1e-30))) - 7)
+    assert np.all(np.abs(o - o_ref) <= O_TOL + ulp)
+    assert float(np.max(np.abs(lse.cpu().numpy() - l_ref))) <= LSE_TOL
+
+
+def test_chunked_prompt_matches_single_pass():
+    # One 300-token prompt in one pass vs three SplitFuse chunks (ctx grows).
+    p, hq, hkv, d, b = 300, 8, 2, 128, 64
+    rng = np.random.default_rng(31)
+    q = wl.bf16_round(rng.standard_normal((p, hq, d)).astype(np.float32))
+    k = wl.bf16_round(rng.standard_normal((p, hkv, d)).astype(np.float32))
+    v = wl.bf16_round(rng.standard_normal((p, hkv, d)).astype(np.float32))
+    table = np.array([[4, 0, 2, 7, 1]], np.int32)
+    one = wl.PassSpec("one", hq, hkv, d, b, 8, np.array([p], np.int32), np.array([0], np.int32),
+                      table, 0)
+    kp, vp = G.gpu_pools(one)
+    t_one = wl.PassTensors(q=q, k_new=k, v_new=v, hist_k=k[:0], hist_v=v[:0])
+    out1, lse1, _ = G.run_pass(one, t_one, kp, vp)
+    kp, vp = G.gpu_pools(one)
+    outs, lses, start = [], [], 0
+    for n in (37, 200, 63):
+        spec = wl.PassSpec("chunk", hq, hkv, d, b, 8, np.array([n], np.int32),
+                           np.array([start], np.int32), table, 0)
+        tc = wl.PassTensors(q=q[start:start + n], k_new=k[start:start + n], v_new=v[start:start + n],
+                            hist_k=k[:0], hist_v=v[:0])
+        o, l_, _ = G.run_pass(spec, tc, kp, vp)
+        outs.append(o)
+        lses.append(l_)
+        start += n
+    assert float((torch.cat(outs) - out1).abs().max()) <= 1e-3
+    assert float((torch.cat(lses) - lse1).abs().max()) <= 1e-3
+
+
+def test_empty_pass_launches_nothing():
+    plan = fgb.Plan([], [], np.zeros((0, 1), np.int32), 4, 4, 64, 16, 8, target_cus=0)
+    meta = plan.upload()
+    kp = torch.zeros((8, 4, 16, 64), dtype=torch.bfloat16, device="cuda")
+    vp = torch.zeros((8, 4, 64, 16), dtype=torch.bfloat16, device="cuda")
+    e = torch.empty((0, 4, 64), dtype=torch.bfloat16, device="cuda")
+    fgb.kv_append(plan, meta, e, e, kp, vp)
+    fgb.attention_ragged(plan, meta, e, kp, vp, torch.empty((0, 4, 64), device="cuda"))
+    torch.cuda.synchronize()
+
+
+def test_workspace_too_small_is_rejected():
+    spec = SMALL_SPECS["mha_d128_b64_mixed"]()
+    tens = wl.make_tensors(spec)
+    kp, vp = G.gpu_pools(spec)
+    plan = fgb.Plan.from_spec(spec, force_splits=3)
+    meta = plan.upload()
+    ws = torch.empty(plan.info["workspace_bytes"] - 16, dtype=torch.uint8, device="cuda")
+    out = torch.empty((spec.num_tokens, spec.num_q_heads, spec.head_dim), device="cuda")
+    with pytest.raises(fgb.FgError) as e:
+        fgb.attention_ragged(plan, meta, G.to_dev(tens.q), kp, vp, out, workspace=ws)
+    assert e.value.status == fgb.FG_E_WORKSPACE
+
+
+# ---------------------------------------------------------------- full-size workloads
+
+@pytest.mark.parametrize("name", ["7b_pass2048", "70b_share4096"])
+def test_full_size_mixed_pass_all_rows(name):
+    spec = wl.config_spec(name)
+    _log(f"[case] full {name} S={spec.num_seqs} T={spec.num_tokens}")
+    tens, _, _, out, lse, plan = G.full_gpu_pass(spec)
+    _log(f"[plan] {plan.info}")
+    o_ref, l_ref = G.oracle_pass(spec, tens)
+    compare(out, lse, o_ref, l_ref, name)
+
+
+def test_full_size_decode64_sampled_sequences():
+    spec = wl.config_spec(3)
+    _log(f"[case] full 7b_decode64 kv={int(spec.kv_lens.sum())}")
+    tens, _, _, out, lse, plan = G.full_gpu_pass(spec)
+    _log(f"[plan] {plan.info}")
+    order = np.argsort(spec.kv_lens)
+    picks = sorted({int(order[-1]), int(order[-2]), int(order[0]), int(order[len(order) // 2]), 5, 17})
+    sub, st, rows = G.subset(spec, tens, picks)
+    o_ref, l_ref = G.oracle_pass(sub, st)
+    compare(out, lse, o_ref, l_ref, f"7b_decode64 seqs {picks}", rows=rows)

@@ -1,0 +1,117 @@
+"""Host planner (fg_plan_pass) on the CPU: validation, coverage, determinism."""
+import numpy as np
+import pytest
+
+from ragged_paged_attention_splitfuse_amd import binding as fgb
+from ragged_paged_attention_splitfuse_amd import workloads as wl
+from tests._plan_check import check_plan
+
+CUS = 256
+
+
+def plan_of(spec, **knobs):
+    knobs.setdefault("target_cus", CUS)
+    return fgb.Plan.from_spec(spec, **knobs)
+
+
+@pytest.mark.parametrize("name", ["tiny", "7b_pass2048", "7b_decode64", "70b_share4096",
+                                  "7b_decode16", "7b_chunk2032", "70b_chunks"])
+def test_plan_covers_every_row_once(name):
+    spec = wl.config_spec(name)
+    check_plan(plan_of(spec), spec)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 7, 64])
+def test_forced_splits_cover(k):
+    spec = wl.custom_spec("f", [1, 300, 2, 1, 70], [2000, 40, 900, 0, 129], 8, 2, 128, 64, seed=3)
+    plan = plan_of(spec, force_splits=k)
+    meta = check_plan(plan, spec)
+    assert plan.info["max_splits_used"] <= k
+    if k > 1:
+        assert len(meta["merges"]) > 0
+
+
+def test_mixed_shapes_and_block_sizes_cover():
+    for d in (64, 128):
+        for b in (16, 32, 64):
+            for hq, hkv in ((4, 4), (8, 2), (12, 4), (6, 1)):
+                spec = wl.custom_spec("m", [1, 5, 130, 1, 3], [77, 0, 260, 5000, 1], hq, hkv, d, b, seed=b + d)
+                check_plan(plan_of(spec), spec)
+                check_plan(plan_of(spec, force_splits=5), spec)
+
+
+def test_plan_is_deterministic():
+    spec = wl.config_spec(3)
+    a, b = plan_of(spec), plan_of(spec)
+    assert np.array_equal(a.metadata()["raw"], b.metadata()["raw"])
+    assert a.info == b.info
+
+
+def test_plan_depends_on_lengths_not_block_ids():
+    spec = wl.config_spec(2)
+    perm = np.random.default_rng(1).permutation(spec.num_blocks).astype(np.int32)
+    spec2 = wl.PassSpec(**{**spec.__dict__})
+    spec2.block_tables = np.where(spec.block_tables >= 0, perm[spec.block_tables], -1).astype(np.int32)
+    ia, ib = plan_of(spec).metadata()["items"], plan_of(spec2).metadata()["items"]
+    assert np.array_equal(ia, ib)
+
+
+def test_long_decodes_are_split_short_ones_not():
+    spec = wl.custom_spec("d", [1] * 64, [16000] + [512] * 63, 32, 32, 128, 64, seed=4)
+    meta = plan_of(spec).metadata()
+    items = meta["items"]
+    per_seq = np.bincount(items[:, 0], minlength=64)
+    assert per_seq[0] > per_seq[1:].max()
+    assert per_seq[1:].max() == 32     # one item per head, no split
+
+
+def test_items_are_longest_first():
+    spec = wl.config_spec(3)
+    items = plan_of(spec).metadata()["items"]
+    lengths = items[:, 5] - items[:, 4]
+    assert np.all(np.diff(lengths) <= 0)
+
+
+def test_tiny_plan_has_no_splits_and_no_workspace():
+    plan = plan_of(wl.config_spec(1))
+    assert plan.info["num_merge_groups"] == 0 and plan.info["workspace_bytes"] == 0
+
+
+def test_empty_pass():
+    plan = fgb.Plan([], [], np.zeros((0, 1), np.int32), 4, 4, 64, 16, 8, target_cus=CUS)
+    assert plan.info["num_tokens"] == 0 and plan.info["num_items"] == 0
+
+
+def _expect(status, **over):
+    base = dict(q_lens=[3, 1], ctx_lens=[0, 20], block_tables=[[0, -1], [1, 2]],
+                num_q_heads=4, num_kv_heads=2, head_dim=128, block_size=16, num_blocks=4,
+                target_cus=CUS)
+    base.update(over)
+    with pytest.raises(fgb.FgError) as e:
+        fgb.Plan(**base)
+    assert e.value.status == status
+
+
+def test_validation_errors():
+    _expect(fgb.FG_E_RANGE, block_tables=[[0, -1], [1, 7]])          # block id out of range
+    _expect(fgb.FG_E_RANGE, block_tables=[[0, -1], [-1, 2]])         # negative id in use
+    _expect(fgb.FG_E_ALIAS, block_tables=[[1, -1], [1, 2]])          # block shared
+    _expect(fgb.FG_E_RANGE, ctx_lens=[0, 40])                        # table too short
+    _expect(fgb.FG_E_RANGE, q_lens=[0, 1])                           # empty query
+    _expect(fgb.FG_E_RANGE, ctx_lens=[-1, 20])
+    _expect(fgb.FG_E_INVALID, num_q_heads=6, num_kv_heads=4)         # Hq % Hkv
+    _expect(fgb.FG_E_UNSUPPORTED, head_dim=96)
+    _expect(fgb.FG_E_UNSUPPORTED, block_size=128)
+    _expect(fgb.FG_E_INVALID, num_blocks=0)
+    _expect(fgb.FG_E_INVALID, scale=float("nan"))
+    _expect(fgb.FG_E_INVALID, scale=-1.0)
+    _expect(fgb.FG_E_INVALID, force_splits=1000)
+    _expect(fgb.FG_E_INVALID, target_cus=-3)
+
+
+def test_unused_table_entries_are_ignored():
+    # entries past ceil(kv/B) may be anything, even out of range or repeated
+    plan = fgb.Plan([3, 1], [0, 20], [[0, 99], [1, 2]], 4, 2, 128, 16, 4, target_cus=CUS)
+    assert plan.info["num_tokens"] == 4
+    plan = fgb.Plan([3, 1], [0, 5], [[0, 1], [1, 2]], 4, 2, 128, 16, 4, target_cus=CUS)
+    assert plan.info["num_tokens"] == 4
