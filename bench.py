@@ -110,6 +110,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="7b_pass2048")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--target-cus", type=int, default=0,
+                    help="planner balance target (0 = the device's CU count)")
     ap.add_argument("--cold-iters", type=int, default=10,
                     help="extra passes timed with a 1 GiB cache flush before each")
     args = ap.parse_args()
@@ -154,7 +156,8 @@ def main():
     out = torch.empty((t, hq, d), dtype=torch.float32, device=dev)
     lse = torch.empty((t, hq), dtype=torch.float32, device=dev)
 
-    probe = fgb.Plan.from_spec(spec)
+    knobs = {"target_cus": args.target_cus}
+    probe = fgb.Plan.from_spec(spec, **knobs)
     info = probe.info
     meta = torch.empty(max(16, info["metadata_bytes"]), dtype=torch.uint8, device=dev)
     ws = torch.empty(max(16, info["workspace_bytes"]), dtype=torch.uint8, device=dev)
@@ -164,7 +167,7 @@ def main():
 
     def step(keep):
         h0 = time.perf_counter()
-        plan = fgb.Plan.from_spec(spec)
+        plan = fgb.Plan.from_spec(spec, **knobs)
         host_plan_s.append(time.perf_counter() - h0)
         plan.upload(meta, stream)
         fgb.kv_append(plan, meta, kn, vn, kp, vp, stream)

@@ -175,9 +175,10 @@ int32_t fg_abi_version(void);
  *   run       4 ints: first new-token row, first slot, token count, block
  *   item      8 ints: seq, kv_head, row0, nrows, kv0, kv1, slot (-1 = final
  *                     rows, else first partial row), waves (0 = vector-ALU path)
- *   merge     8 ints: seq, kv_head, row0, nrows, nsplit, slot0, 0, 0
+ *   merge     8 ints: seq, kv_head, row0, nrows, nsplit, slot0, r_begin, r_count
  * Packed row r of an item is query token r / G at q head kv_head * G + r % G;
- * split i of a merge group's row r sits at partial row slot0 + i * nrows + r.
+ * split i of a split group's row r sits at partial row slot0 + i * nrows + r;
+ * a merge record covers rows r_begin .. r_begin + r_count - 1 of its group.
  * host_dst may be NULL to query the layout only. */
 typedef struct fg_plan_layout_t {
   int64_t seqs, block_ids, runs, items, merges;   /* byte offsets */

@@ -46,6 +46,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
+// Reference-max slack of the matrix-core path's online softmax (log2 units).
+constexpr float kRescaleSlack = 8.f;
 
 struct AttnArgs {
   const SeqRec* seqs;
@@ -439,6 +441,13 @@ __device__ void mfma_item(const AttnArgs& a, const ItemRec& it, uint16_t* lds) {
     }
   };
 
+  // Causal limit of the wave's first packed row: a stage ending at or below it,
+  // and inside the item's range, needs no mask for any row of the wave.
+  const int lim_lo = sq.ctx + (it.row0 + wave * kMfmaRowsPerWave) / G;
+  const float c = a.scale_log2;
+  constexpr uint32_t kOnePair = 0x3F803F80u;  // two bf16 1.0
+  float lrnd = 0.f;  // row sum of the bf16-rounded probabilities
+
   load_stage(it.kv0);
   store_stage(0);
   __syncthreads();
@@ -460,34 +469,61 @@ __device__ void mfma_item(const AttnArgs& a, const ItemRec& it, uint16_t* lds) {
           sacc[h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[kk], sacc[h2], 0, 0, 0);
         }
       }
+      // raw scores; masked ones become -inf (only in boundary stages)
       float mt = -INFINITY;
+      if (tb + kKvTile > it.kv1 || tb + kKvTile - 1 > lim_lo) {
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
+        for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int tok = tb + 32 * h2 + 16 * (v >> 3) + 8 * hf + (v & 7);
-          const float x = (tok < it.kv1 && tok <= lim) ? sacc[h2][v] * a.scale_log2 : -INFINITY;
-          sacc[h2][v] = x;
-          mt = fmaxf(mt, x);
-        }
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float mn = fmaxf(m, mt);
-      const float mref = (mn == -INFINITY) ? 0.f : mn;
-      const float alpha = fast_exp2(m - mref);
-      float ps = 0.f;
+          for (int v = 0; v < 16; ++v) {
+            const int tok = tb + 32 * h2 + 16 * (v >> 3) + 8 * hf + (v & 7);
+            const float x = (tok < it.kv1 && tok <= lim) ? sacc[h2][v] : -INFINITY;
+            sacc[h2][v] = x;
+            mt = fmaxf(mt, x);
+          }
+      } else {
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) mt = fmaxf(mt, sacc[h2][v]);
+      }
+      mt = fmaxf(mt, __shfl_xor(mt, 32)) * c;
+      // Lazy rescale: the reference max m moves only when a row's stage max
+      // exceeds it by more than kRescaleSlack (log2 units), so probabilities
+      // stay <= 2^kRescaleSlack and most stages skip the O rescale.
+      if (__any(mt > m + kRescaleSlack)) {
+        const float mn = fmaxf(m, mt);
+        const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(m - mn);
+        lsum *= alpha;
+        lrnd *= alpha;
+#pragma unroll
+        for (int dd = 0; dd < D / 32; ++dd) o[dd] *= alpha;
+        m = mn;
+      }
+      const float mref = (m == -INFINITY) ? 0.f : m;
+      // Probabilities: the fp32 row sum feeds the LSE; the bf16-rounded P^T
+      // operand of the P V product is summed as well (v_dot2 against 1.0), and
+      // O is normalised by that sum, so it is an exact convex combination of V
+      // rows under the weights actually used.
       bf16x8 pb[2][2];
+      float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const float p = fast_exp2(sacc[h2][v] - mref);
-          ps += p;
+          const float p = fast_exp2(fmaf(sacc[h2][v], c, -mref));
+          if (v & 1) ps1 += p; else ps0 += p;
           pb[h2][v >> 3][v & 7] = __bf16(p);
         }
-      lsum = lsum * alpha + ps;
-      m = mn;
+      lsum += ps0 + ps1;
 #pragma unroll
-      for (int dd = 0; dd < D / 32; ++dd) o[dd] *= alpha;
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const u32x4 w = __builtin_bit_cast(u32x4, pb[h2][ks]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) lrnd = dot2(w[e], kOnePair, lrnd);
+        }
 #pragma unroll
       for (int dd = 0; dd < D / 32; ++dd)
 #pragma unroll
@@ -505,7 +541,8 @@ __device__ void mfma_item(const AttnArgs& a, const ItemRec& it, uint16_t* lds) {
 
   if (active) {
     const float lt = lsum + __shfl_xor(lsum, 32);
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float lr = lrnd + __shfl_xor(lrnd, 32);
+    const float inv = lr > 0.f ? 1.f / lr : 0.f;
     const float lse_val = lt > 0.f ? (m + fast_log2(lt)) * kLn2 : -INFINITY;
     if (row_ok) {
 #pragma unroll
@@ -529,7 +566,7 @@ constexpr int valu_lds_bytes() {
 }
 
 template <int D, int B, bool MFMA>
-__global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   constexpr int kLds = MFMA ? (MfmaLds<D>::BYTES > valu_lds_bytes<D>() ? MfmaLds<D>::BYTES
                                                                         : valu_lds_bytes<D>())
                             : valu_lds_bytes<D>();
@@ -547,9 +584,32 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     valu_item<D, B, kValuMaxRows>(a, it, reinterpret_cast<float*>(smem));
 }
 
+// One wavefront per merged row; lane holds D/64 consecutive dims.
 template <int D>
 __global__ __launch_bounds__(kThreads) void merge_kernel(AttnArgs a, const MergeRec* merges) {
+  constexpr int PL = D / 64;
   const MergeRec mg = merges[blockIdx.x];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (wave >= mg.r_count) return;
+  const int r = mg.r_begin + wave;
+  float mx = -INFINITY;
+  for (int i = 0; i < mg.nsplit; ++i) mx = fmaxf(mx, a.ws_lse[mg.slot0 + i * mg.nrows + r]);
+  float wsum = 0.f, acc[PL];
+#pragma unroll
+  for (int e = 0; e < PL; ++e) acc[e] = 0.f;
+#pragma unroll 4
+  for (int i = 0; i < mg.nsplit; ++i) {
+    const int pr = mg.slot0 + i * mg.nrows + r;
+    const float li = a.ws_lse[pr];
+    const float w = (li == -INFINITY) ? 0.f : fast_exp2((li - mx) * kLog2e);
+    wsum += w;
+    const float* src = a.ws_o + size_t(pr) * D + PL * lane;
+#pragma unroll
+    for (int e = 0; e < PL; ++e) acc[e] = fmaf(w, src[e], acc[e]);
+  }
+  const float inv = 1.f / wsum;
+#pragma unroll
+  for (int e = 0; e < PL; ++e) acc[e] *= inv;
   const SeqRec sq = a.seqs[mg.seq];
   ItemRec it;
   it.seq = mg.seq;
@@ -557,22 +617,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnArgs a, const Merge
   it.row0 = mg.row0;
   it.nrows = mg.nrows;
   it.slot = -1;
-  for (int idx = threadIdx.x; idx < mg.nrows * D; idx += kThreads) {
-    const int r = idx / D, d = idx % D;
-    float mx = -INFINITY;
-    for (int i = 0; i < mg.nsplit; ++i) mx = fmaxf(mx, a.ws_lse[mg.slot0 + i * mg.nrows + r]);
-    float wsum = 0.f, os = 0.f;
-    for (int i = 0; i < mg.nsplit; ++i) {
-      const int pr = mg.slot0 + i * mg.nrows + r;
-      const float li = a.ws_lse[pr];
-      const float w = (li == -INFINITY) ? 0.f : fast_exp2((li - mx) * kLog2e);
-      wsum += w;
-      os += w * a.ws_o[size_t(pr) * D + d];
-    }
-    const float o = os / wsum;
-    const float lse_val = mx + fast_log2(wsum) * kLn2;
-    store_result(a, sq, it, D, r, d, &o, 1, d == 0, lse_val);
-  }
+  store_result(a, sq, it, D, r, PL * lane, acc, PL, lane == 0, mx + fast_log2(wsum) * kLn2);
 }
 
 template <int D, int B>

@@ -53,8 +53,11 @@ struct ItemRec {
   int32_t waves;     // matrix-core path: active wavefronts (1..4); else 0
 };
 
-// One merge group: `nsplit` partials of `nrows` rows each, split i of row r at
-// partial row slot0 + i * nrows + r.
+// Rows of a split group: the group has `nsplit` partials of `nrows` rows each,
+// split i of row r at partial row slot0 + i * nrows + r.  One record covers
+// rows [r_begin, r_begin + r_count) of the group, r_count <= kMergeRowsPerRec
+// (one wavefront per row).
+constexpr int kMergeRowsPerRec = 4;
 struct MergeRec {
   int32_t seq;
   int32_t kv_head;
@@ -62,7 +65,8 @@ struct MergeRec {
   int32_t nrows;
   int32_t nsplit;
   int32_t slot0;
-  int32_t pad0, pad1;
+  int32_t r_begin;
+  int32_t r_count;
 };
 
 static_assert(sizeof(SeqRec) == 32, "SeqRec layout");

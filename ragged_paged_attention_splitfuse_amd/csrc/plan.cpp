@@ -36,10 +36,18 @@ constexpr int64_t kMaxKvLen = int64_t(1) << 28;
 constexpr int kDefaultMinSplitTokens = 256;
 constexpr int kDefaultMaxSplits = 64;
 constexpr int kMaxSplitsLimit = 256;
-// Concurrent work-groups per CU assumed by the balance target, and how many
-// items each such slot should receive at least.
-constexpr int kSlotsPerCu = 2;
-constexpr int kItemsPerSlot = 4;
+// Work items each CU should receive at least: items longer than
+// total / (CUs * kItemsPerCu) are split, so longest-first dispatch ends with
+// every CU busy until close to the mean.
+constexpr double kItemsPerCu = 4.0;
+// Matrix-core tiles: relative cost per KV token of a tile with R padded rows
+// is max(kMfmaMinCost, R / kFlopPerByte), where kFlopPerByte is the ratio of
+// achievable bf16 MFMA rate to achievable HBM rate on MI355X (about
+// 1000 TFLOP/s : 6 TB/s).  A split of a tile also moves its partial rows
+// through the workspace, so tiles are not split below kMfmaMinSplitTokens.
+constexpr double kFlopPerByte = 170.0;
+constexpr double kMfmaMinCost = 0.5;
+constexpr int kMfmaMinSplitTokens = 512;
 
 size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -165,7 +173,9 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
             const int j_last = (r0 + nr - 1) / G;
             const int vis = r.ctx + j_last + 1;
             const int waves = (nr + fg::kMfmaRowsPerWave - 1) / fg::kMfmaRowsPerWave;
-            Group grp{s, g, r0, nr, vis, waves, double(vis)};
+            const double per_tok =
+                std::max(kMfmaMinCost, double(waves * fg::kMfmaRowsPerWave) / kFlopPerByte);
+            Group grp{s, g, r0, nr, vis, waves, per_tok * double(vis)};
             groups.push_back(grp);
             total_cost += grp.cost;
           }
@@ -174,11 +184,11 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
     }
 
     // ---- split each group's visible range [0, vis_end)
-    const double target =
-        std::max(1.0, total_cost / double(int64_t(target_cus) * kSlotsPerCu * kItemsPerSlot));
+    const double target = std::max(1.0, total_cost / (double(target_cus) * kItemsPerCu));
     std::vector<Pending> mfma, valu;
     std::vector<MergeRec> merges;
     int64_t partial_rows = 0;
+    int32_t merge_groups = 0;
     int max_used = 1;
     int32_t order = 0;
     for (const Group& grp : groups) {
@@ -188,7 +198,8 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
       } else {
         k = int64_t(ceil(grp.cost / target));
         k = std::min<int64_t>(k, max_splits);
-        k = std::min<int64_t>(k, std::max<int64_t>(1, grp.vis_end / std::max(1, min_split)));
+        const int floor_tokens = grp.waves ? std::max(min_split, kMfmaMinSplitTokens) : min_split;
+        k = std::min<int64_t>(k, std::max<int64_t>(1, grp.vis_end / std::max(1, floor_tokens)));
       }
       k = std::max<int64_t>(1, std::min<int64_t>(k, ceil_div(grp.vis_end, fg::kKvTile)));
       const int64_t chunk = ceil_div(ceil_div(grp.vis_end, k), fg::kKvTile) * fg::kKvTile;
@@ -199,15 +210,19 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
         if (partial_rows + k * grp.nrows > INT32_MAX) return FG_E_RANGE;
         slot0 = int32_t(partial_rows);
         partial_rows += k * grp.nrows;
-        MergeRec m;
-        m.seq = grp.seq;
-        m.kv_head = grp.kv_head;
-        m.row0 = grp.row0;
-        m.nrows = grp.nrows;
-        m.nsplit = int32_t(k);
-        m.slot0 = slot0;
-        m.pad0 = m.pad1 = 0;
-        merges.push_back(m);
+        ++merge_groups;
+        for (int rb = 0; rb < grp.nrows; rb += fg::kMergeRowsPerRec) {
+          MergeRec m;
+          m.seq = grp.seq;
+          m.kv_head = grp.kv_head;
+          m.row0 = grp.row0;
+          m.nrows = grp.nrows;
+          m.nsplit = int32_t(k);
+          m.slot0 = slot0;
+          m.r_begin = rb;
+          m.r_count = std::min(fg::kMergeRowsPerRec, grp.nrows - rb);
+          merges.push_back(m);
+        }
       }
       for (int64_t i = 0; i < k; ++i) {
         Pending p;
@@ -249,6 +264,7 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
     plan->n_valu = int32_t(valu.size());
     plan->n_items = plan->n_mfma + plan->n_valu;
     plan->n_merge = int32_t(merges.size());
+    plan->n_merge_groups = merge_groups;
     plan->n_partial_rows = int32_t(partial_rows);
     plan->max_splits_used = max_used;
     plan->target_cus = target_cus;
@@ -291,7 +307,7 @@ extern "C" fg_status fg_plan_info(const fg_plan* p, fg_plan_info_t* o) {
   o->num_items = p->n_items;
   o->num_valu_items = p->n_valu;
   o->num_mfma_items = p->n_mfma;
-  o->num_merge_groups = p->n_merge;
+  o->num_merge_groups = p->n_merge_groups;
   o->num_partial_rows = p->n_partial_rows;
   o->max_splits_used = p->max_splits_used;
   o->num_append_runs = p->n_runs;

@@ -25,7 +25,8 @@ struct fg_plan {
   int32_t n_items = 0;   // n_mfma matrix-core items first, then n_valu
   int32_t n_mfma = 0;
   int32_t n_valu = 0;
-  int32_t n_merge = 0;
+  int32_t n_merge = 0;          // merge records (<= kMergeRowsPerRec rows each)
+  int32_t n_merge_groups = 0;   // row groups that were split
   int32_t n_partial_rows = 0;
   int32_t max_splits_used = 0;
   int32_t target_cus = 0;

@@ -43,11 +43,15 @@ def check_plan(plan, spec):
         groups[(seq, kvh, row0, nrows)].append((kv0, kv1, slot))
 
     merge_by_group = {}
+    merge_rows = defaultdict(list)
     for m in merges:
-        seq, kvh, row0, nrows, nsplit, slot0 = map(int, m[:6])
+        seq, kvh, row0, nrows, nsplit, slot0, r_begin, r_count = map(int, m)
         key = (seq, kvh, row0, nrows)
-        assert key not in merge_by_group
-        merge_by_group[key] = (nsplit, slot0)
+        assert merge_by_group.setdefault(key, (nsplit, slot0)) == (nsplit, slot0)
+        assert 1 <= r_count <= 4 and 0 <= r_begin and r_begin + r_count <= nrows
+        merge_rows[key].extend(range(r_begin, r_begin + r_count))
+    for key, rows in merge_rows.items():
+        assert sorted(rows) == list(range(key[3]))
 
     used_slots = np.zeros(info["num_partial_rows"], dtype=np.int32)
     rows_seen = defaultdict(int)

@@ -22,6 +22,9 @@ pytestmark = pytest.mark.gpu
 
 O_TOL = 1e-2
 LSE_TOL = 1e-3
+# Split vs unsplit on the GPU: both round P to bf16, but against different
+# reference maxima, so each carries its own (independent) rounding error.
+SPLIT_O_TOL = 5e-3
 
 
 def _log(msg):
@@ -88,8 +91,9 @@ def test_forced_split_counts(k):
     o_ref, l_ref = G.oracle_pass(spec, tens)
     compare(out, lse, o_ref, l_ref, f"force_splits={k}")
     _, _, _, out1, lse1, _ = G.full_gpu_pass(spec, tens=tens, force_splits=1)
-    assert float((out - out1).abs().max()) <= 1e-3
-    assert float((lse - lse1).abs().max()) <= 1e-3
+    do, dl = float((out - out1).abs().max()), float((lse - lse1).abs().max())
+    _log(f"[split-invariance] k={k}: max|dO|={do:.3e} max|dLSE|={dl:.3e}")
+    assert do <= SPLIT_O_TOL and dl <= LSE_TOL
 
 
 def test_forced_splits_gqa_tiles():
