@@ -114,6 +114,9 @@ def main():
                     help="planner balance target (0 = the device's CU count)")
     ap.add_argument("--cold-iters", type=int, default=10,
                     help="extra passes timed with a 1 GiB cache flush before each")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one device-to-device copy of this many MiB (a known-size "
+                         "kernel that calibrates HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -272,6 +275,15 @@ def main():
             "kernel_source_sha256_16": source_hash(),
         },
     }
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        res["detail"]["copy_probe_bytes"] = {"read": n, "write": n}
+        del src, dst
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(spec, tens)
         res["detail"]["gpu_vs_oracle"] = round(res["cpu_baseline"]["value"] / pass_us, 1)

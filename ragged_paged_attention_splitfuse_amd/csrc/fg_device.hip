@@ -398,28 +398,57 @@ __device__ void mfma_item(const AttnArgs& a, const ItemRec& it, uint16_t* lds) {
   const size_t kv_head_base = size_t(g);
   u32x4 kst[KCH], vst[VCH];
 
+  // Global -> register staging of one 64-token stage.  Chunk c of this thread
+  // is 16-byte chunk ch = tid + 256 c of the stage.  With B == 64 a stage is
+  // exactly one block, and both its K rows and its V^T rows are one contiguous
+  // region of the block, so chunk ch sits at element offset 8 * ch of it.
+  // Only the final stage of a sequence (past kv_len) needs bounds checks.
   auto load_stage = [&](int tb) {
-    int blk_u = 0;
-    if constexpr (B >= kKvTile) blk_u = bt[tb / B];
+    const bool full = tb + kKvTile <= kv_valid;
+    if constexpr (B == kKvTile) {
+      const size_t tile = (size_t(bt[tb / B]) * a.hkv + kv_head_base) * (size_t(B) * D);
+      const uint16_t* kb = a.kpool + tile;
+      const uint16_t* vb = a.vpool + tile;
+      if (full) {
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-      const int ch = tid + kThreads * c;
-      const int tok = ch / CPR, dc = ch % CPR, p = tb + tok;
-      kst[c] = u32x4{0u, 0u, 0u, 0u};
-      if (p < kv_valid) {
-        const int blk = (B >= kKvTile) ? blk_u : bt[p / B];
-        kst[c] = ld16(a.kpool + ((size_t(blk) * a.hkv + kv_head_base) * B + p % B) * D + 8 * dc);
+        for (int c = 0; c < KCH; ++c) kst[c] = ld16(kb + 8 * (tid + kThreads * c));
+#pragma unroll
+        for (int c = 0; c < VCH; ++c) vst[c] = ld16(vb + 8 * (tid + kThreads * c));
+        return;
       }
-    }
 #pragma unroll
-    for (int c = 0; c < VCH; ++c) {
-      const int ch = tid + kThreads * c;
-      const int d = ch / (kKvTile / 8), tc = ch % (kKvTile / 8), p = tb + 8 * tc;
-      vst[c] = u32x4{0u, 0u, 0u, 0u};
-      if (p < kv_valid) {
-        const int blk = (B >= kKvTile) ? blk_u : bt[p / B];
-        vst[c] = ld16(a.vpool + ((size_t(blk) * a.hkv + kv_head_base) * D + d) * B + p % B);
-        if (p + 8 > kv_valid) vst[c] = zero_tail(vst[c], p, kv_valid);
+      for (int c = 0; c < KCH; ++c) {
+        const int ch = tid + kThreads * c;
+        kst[c] = (tb + ch / CPR < kv_valid) ? ld16(kb + 8 * ch) : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int c = 0; c < VCH; ++c) {
+        const int ch = tid + kThreads * c;
+        const int p = tb + 8 * (ch % (kKvTile / 8));
+        vst[c] = (p < kv_valid) ? zero_tail(ld16(vb + 8 * ch), p, kv_valid) : u32x4{0u, 0u, 0u, 0u};
+      }
+    } else {
+      // B < 64: the stage spans 64 / B blocks; resolve each chunk's block.
+#pragma unroll
+      for (int c = 0; c < KCH; ++c) {
+        const int ch = tid + kThreads * c;
+        const int tok = ch / CPR, dc = ch % CPR, p = tb + tok;
+        kst[c] = u32x4{0u, 0u, 0u, 0u};
+        if (full || p < kv_valid) {
+          const int blk = bt[p / B];
+          kst[c] = ld16(a.kpool + ((size_t(blk) * a.hkv + kv_head_base) * B + p % B) * D + 8 * dc);
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < VCH; ++c) {
+        const int ch = tid + kThreads * c;
+        const int d = ch / (kKvTile / 8), tc = ch % (kKvTile / 8), p = tb + 8 * tc;
+        vst[c] = u32x4{0u, 0u, 0u, 0u};
+        if (full || p < kv_valid) {
+          const int blk = bt[p / B];
+          vst[c] = ld16(a.vpool + ((size_t(blk) * a.hkv + kv_head_base) * D + d) * B + p % B);
+          if (!full && p + 8 > kv_valid) vst[c] = zero_tail(vst[c], p, kv_valid);
+        }
       }
     }
   };
@@ -573,7 +602,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kLds];
   const ItemRec it = a.items[blockIdx.x];
   if constexpr (MFMA) {
-    if (int(blockIdx.x) < a.n_mfma) {
+    if (it.waves > 0) {
       mfma_item<D, B>(a, it, reinterpret_cast<uint16_t*>(smem));
       return;
     }

@@ -17,7 +17,7 @@ def check_plan(plan, spec):
     g_ratio = spec.num_q_heads // spec.num_kv_heads
     info = plan.info
     assert len(items) == info["num_items"] == info["num_mfma_items"] + info["num_valu_items"]
-    n_mfma = info["num_mfma_items"]
+    assert int((items[:, 7] > 0).sum()) == info["num_mfma_items"]
 
     # per-sequence records
     q_start = 0
@@ -36,10 +36,10 @@ def check_plan(plan, spec):
         seq, kvh, row0, nrows, kv0, kv1, slot, waves = map(int, it)
         assert 0 <= seq < spec.num_seqs and 0 <= kvh < spec.num_kv_heads
         assert nrows >= 1 and kv1 > kv0 >= 0 and kv0 % 64 == 0
-        if idx < n_mfma:
+        if waves > 0:
             assert waves == -(-nrows // 32) and nrows <= 128
         else:
-            assert nrows <= 4 and waves == 0
+            assert nrows <= 4
         groups[(seq, kvh, row0, nrows)].append((kv0, kv1, slot))
 
     merge_by_group = {}
