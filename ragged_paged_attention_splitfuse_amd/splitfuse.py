@@ -1,0 +1,161 @@
+"""Host Dynamic SplitFuse scheduler and paged-KV block allocator (trace replay).
+
+Composes forward passes from a request trace at a fixed token budget, the
+pass-composition strategy of "DeepSpeed-FastGen: High-throughput Text
+Generation for LLMs via MII and DeepSpeed-Inference" (research summary,
+"Summary" and idea I3): every request that is generating contributes one
+decode token, and prompt tokens fill the rest of the budget exactly -- long
+prompts are cut into chunks spread over several passes, short ones are packed
+together.  Requests come from closed-loop clients, as in the benchmark setup
+of the same page ("Key points": 1-32 clients, 512 requests, prompt and output
+lengths normal with means 2600 and 60).
+
+Readings where the pages leave the policy open (any composition gives the
+same attention results, so none of this is parity-checked):
+* decodes first, then prompt chunks FIFO by admission, the in-progress prompt
+  first, several prompts fused when room remains;
+* a request with output length O needs O - 1 decode passes: its first output
+  token comes from the last prompt position;
+* 32 closed-loop clients: a client submits its next request in the pass after
+  its previous one finished;
+* KV blocks come from a seeded, shuffled free list, are allocated on demand
+  and returned to the back of the list when a request finishes.
+
+This module only composes passes (lengths, positions, block tables); the
+attention itself runs through the C-ABI library.
+"""
+from dataclasses import dataclass
+
+import numpy as np
+
+
+@dataclass
+class TraceRequest:
+    rid: int
+    prompt: int
+    output: int
+
+
+def trace_requests(n=512, seed=5, prompt_mean=2600.0, prompt_sd=780.0, out_mean=60.0, out_sd=18.0):
+    """Synthetic request trace: lengths clamped >= 1."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    p = np.maximum(1, np.rint(rng.normal(prompt_mean, prompt_sd, n))).astype(np.int64)
+    o = np.maximum(1, np.rint(rng.normal(out_mean, out_sd, n))).astype(np.int64)
+    return [TraceRequest(i, int(p[i]), int(o[i])) for i in range(n)]
+
+
+@dataclass
+class ScheduledPass:
+    index: int
+    rids: np.ndarray         # int64 [S] request per sequence, decodes first
+    q_lens: np.ndarray       # int32 [S]
+    ctx_lens: np.ndarray     # int32 [S]
+    block_tables: np.ndarray  # int32 [S, width], unused -1
+    num_decodes: int
+
+    @property
+    def num_tokens(self):
+        return int(self.q_lens.sum())
+
+
+class _Live:
+    __slots__ = ("req", "prompt_done", "decodes_done", "blocks", "admitted")
+
+    def __init__(self, req, admitted):
+        self.req = req
+        self.prompt_done = 0
+        self.decodes_done = 0
+        self.blocks = []
+        self.admitted = admitted
+
+
+def compose(requests, clients=32, budget=2048):
+    """Pass composition only: list of [(rid, ctx, q_len, is_decode), ...]."""
+    pending = list(requests)
+    live = []
+    order = 0
+    passes = []
+    for _ in range(min(clients, len(pending))):
+        live.append(_Live(pending.pop(0), order))
+        order += 1
+    while live:
+        seqs = []
+        for lv in live:
+            if lv.prompt_done == lv.req.prompt and lv.decodes_done < lv.req.output - 1:
+                seqs.append((lv, lv.req.prompt + lv.decodes_done, 1, True))
+        left = budget - len(seqs)
+        if left < 0:
+            raise ValueError("more decodes than the token budget")
+        for lv in live:                      # admission order == list order
+            if left == 0:
+                break
+            if lv.prompt_done < lv.req.prompt:
+                n = min(lv.req.prompt - lv.prompt_done, left)
+                seqs.append((lv, lv.prompt_done, n, False))
+                left -= n
+        if not seqs:
+            raise RuntimeError("scheduler made no progress")
+        passes.append([(lv.req.rid, ctx, n, dec) for lv, ctx, n, dec in seqs])
+        finished = []
+        for lv, ctx, n, dec in seqs:
+            if dec:
+                lv.decodes_done += 1
+            else:
+                lv.prompt_done += n
+            if lv.prompt_done == lv.req.prompt and lv.decodes_done == lv.req.output - 1:
+                finished.append(lv)
+        for lv in finished:
+            live.remove(lv)
+            if pending:
+                live.append(_Live(pending.pop(0), order))
+                order += 1
+    return passes
+
+
+def schedule(requests, clients=32, budget=2048, block_size=64, seed=5, slack=1.25):
+    """Compose passes and give every sequence its block table.
+
+    Returns (passes, num_blocks).  The pool holds slack x the peak number of
+    blocks live at once; blocks come from a shuffled free list.
+    """
+    comp = compose(requests, clients, budget)
+    last = {}
+    for i, p in enumerate(comp):
+        for rid, _, _, _ in p:
+            last[rid] = i
+    finals = [[] for _ in comp]
+    for rid, i in last.items():
+        finals[i].append(rid)
+    need, peak = {}, 0
+    for i, p in enumerate(comp):
+        for rid, ctx, n, _ in p:
+            need[rid] = -(-(ctx + n) // block_size)
+        peak = max(peak, sum(need.values()))
+        for rid in finals[i]:
+            del need[rid]
+    num_blocks = int(np.ceil(slack * peak))
+    rng = np.random.Generator(np.random.PCG64(seed))
+    free = [int(b) for b in rng.permutation(num_blocks)]
+    head = 0
+    tables = {}
+    out = []
+    for i, p in enumerate(comp):
+        rows = []
+        for rid, ctx, n, _ in p:
+            t = tables.setdefault(rid, [])
+            while len(t) * block_size < ctx + n:
+                if head >= len(free):
+                    raise RuntimeError("KV pool exhausted")
+                t.append(free[head])
+                head += 1
+            rows.append(t)
+        width = max(len(r) for r in rows)
+        bt = np.full((len(rows), width), -1, dtype=np.int32)
+        for s, r in enumerate(rows):
+            bt[s, :len(r)] = r
+        out.append(ScheduledPass(
+            i, np.array([x[0] for x in p], np.int64), np.array([x[2] for x in p], np.int32),
+            np.array([x[1] for x in p], np.int32), bt, sum(1 for x in p if x[3])))
+        for rid in finals[i]:
+            free.extend(tables.pop(rid))
+    return out, num_blocks

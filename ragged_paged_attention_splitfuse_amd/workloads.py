@@ -260,3 +260,66 @@ def empty_pool_bits(spec, poison=False):
     shape = (spec.num_blocks, spec.num_kv_heads, spec.block_size, spec.head_dim)
     tshape = (spec.num_blocks, spec.num_kv_heads, spec.head_dim, spec.block_size)
     return np.full(shape, fill, np.uint16), np.full(tshape, fill, np.uint16)
+
+
+# ---------------------------------------------------------------- keyed hash generator
+#
+# For request traces the K/V/Q values of a token must not depend on which pass
+# processed it, so they are a pure function of (seed, kind, request, position,
+# head, dim): a counter-based generator built from the 32-bit "lowbias32"
+# integer hash (Chris Wellons' hash-prospector construction:
+# x ^= x >> 16; x *= 0x7feb352d; x ^= x >> 15; x *= 0x846ca68b; x ^= x >> 16).
+# Two hashes give four 16-bit uniforms whose sum (Irwin-Hall, n = 4) is
+# centred and scaled by 2^-15, an approximately normal value with sd ~1.155,
+# then rounded to bf16 nearest-even.  Everything before the final rounding is
+# exact integer arithmetic, and the integer -> float32 conversion and the
+# power-of-two scaling are exact, so the numpy and torch versions below give
+# identical bits on any device.
+
+KIND_Q, KIND_K, KIND_V = 1, 2, 3
+_M32 = 0xFFFFFFFF
+
+
+def _lowbias32(x, xp):
+    x = x ^ (x >> 16)
+    x = (x * 0x7FEB352D) & _M32
+    x = x ^ (x >> 15)
+    x = (x * 0x846CA68B) & _M32
+    x = x ^ (x >> 16)
+    return x
+
+
+def _token_keys(seed, kind, rid, positions, xp):
+    """One 32-bit key per token; rid is a scalar or an array shaped like positions."""
+    k = _lowbias32(positions * 0 + ((seed * 0x9E3779B1 + kind) & _M32), xp)
+    k = _lowbias32(k ^ (rid & _M32), xp)
+    return _lowbias32(k ^ positions, xp)
+
+
+def hash_normal_bf16(seed, kind, rid, positions, heads, head_dim):
+    """numpy: bf16 bits [len(positions), len(heads), head_dim] for one request."""
+    pos = np.asarray(positions, dtype=np.int64)
+    hs = np.asarray(heads, dtype=np.int64)
+    key = _token_keys(seed, kind, rid, pos, np)                      # [n]
+    elem = (hs[:, None] * head_dim + np.arange(head_dim, dtype=np.int64)[None, :]) * 2  # [H, D]
+    x0 = _lowbias32(key[:, None, None] ^ elem[None], np)
+    x1 = _lowbias32(key[:, None, None] ^ (elem[None] + 1), np)
+    u = (x0 & 0xFFFF) + (x0 >> 16) + (x1 & 0xFFFF) + (x1 >> 16) - 131070
+    return bf16_round(u.astype(np.float32) * np.float32(2.0 ** -15))
+
+
+def hash_normal_bf16_torch(seed, kind, rid, positions, num_heads, head_dim, device):
+    """torch (any device): bf16 tensor [len(positions), num_heads, head_dim], same bits.
+
+    rid may be one request id or one per position (a whole pass at once)."""
+    import torch
+    pos = torch.as_tensor(positions, dtype=torch.int64, device=device)
+    if not isinstance(rid, int):
+        rid = torch.as_tensor(rid, dtype=torch.int64, device=device)
+    key = _token_keys(seed, kind, rid, pos, torch)
+    elem = (torch.arange(num_heads, dtype=torch.int64, device=device)[:, None] * head_dim
+            + torch.arange(head_dim, dtype=torch.int64, device=device)[None, :]) * 2
+    x0 = _lowbias32(key[:, None, None] ^ elem[None], torch)
+    x1 = _lowbias32(key[:, None, None] ^ (elem[None] + 1), torch)
+    u = (x0 & 0xFFFF) + (x0 >> 16) + (x1 & 0xFFFF) + (x1 >> 16) - 131070
+    return (u.to(torch.float32) * (2.0 ** -15)).to(torch.bfloat16)

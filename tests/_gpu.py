@@ -105,3 +105,54 @@ def oracle_pass(spec, tens):
     kp, vp = oracle_pools(spec, tens, poison=True)
     return ora.attend(tens.q, kp, vp, spec.q_lens, spec.ctx_lens, spec.block_tables,
                       spec.block_size, spec.num_kv_heads, scale=spec.scale or None)
+
+
+def trace_pass_inputs(p, seed, hq, hkv, d, device="cuda"):
+    """Q, new K, new V of one scheduled pass from the keyed hash generator."""
+    rid_rows = np.repeat(p.rids, p.q_lens)
+    pos_rows = np.concatenate([np.arange(c, c + n) for c, n in zip(p.ctx_lens, p.q_lens)])
+    q = wl.hash_normal_bf16_torch(seed, wl.KIND_Q, rid_rows, pos_rows, hq, d, device)
+    k = wl.hash_normal_bf16_torch(seed, wl.KIND_K, rid_rows, pos_rows, hkv, d, device)
+    v = wl.hash_normal_bf16_torch(seed, wl.KIND_V, rid_rows, pos_rows, hkv, d, device)
+    return q.contiguous(), k.contiguous(), v.contiguous()
+
+
+def trace_oracle(p, seqs, heads, seed, head_dim, block_size):
+    """Oracle rows for sequences `seqs` of a scheduled pass, on q/kv heads `heads`.
+
+    Each sequence's whole history is regenerated from the keyed generator (it
+    does not depend on which pass wrote it), so no GPU data enters the oracle.
+    The sub-pass is MHA over the chosen heads with compact block ids.
+    """
+    hs = list(heads)
+    q_lens = p.q_lens[seqs].astype(np.int32)
+    ctx = p.ctx_lens[seqs].astype(np.int32)
+    qs, kn, vn, hk, hv = [], [], [], [], []
+    for s in seqs:
+        rid, c, n = int(p.rids[s]), int(p.ctx_lens[s]), int(p.q_lens[s])
+        qs.append(wl.hash_normal_bf16(seed, wl.KIND_Q, rid, np.arange(c, c + n), hs, head_dim))
+        k = wl.hash_normal_bf16(seed, wl.KIND_K, rid, np.arange(0, c + n), hs, head_dim)
+        v = wl.hash_normal_bf16(seed, wl.KIND_V, rid, np.arange(0, c + n), hs, head_dim)
+        hk.append(k[:c]); kn.append(k[c:]); hv.append(v[:c]); vn.append(v[c:])
+    spec = wl.custom_spec("trace-sub", q_lens, ctx, len(hs), len(hs), head_dim, block_size,
+                          seed=1, slack=1.0)
+    tens = wl.PassTensors(q=np.concatenate(qs), k_new=np.concatenate(kn), v_new=np.concatenate(vn),
+                          hist_k=np.concatenate(hk), hist_v=np.concatenate(hv))
+    return oracle_pass(spec, tens)
+
+
+def trace_oracle_gqa(p, seqs, q_head, kv_head, seed, head_dim, block_size):
+    """Oracle rows of one q head (which reads kv_head) for sequences `seqs`."""
+    q_lens = p.q_lens[seqs].astype(np.int32)
+    ctx = p.ctx_lens[seqs].astype(np.int32)
+    qs, kn, vn, hk, hv = [], [], [], [], []
+    for s in seqs:
+        rid, c, n = int(p.rids[s]), int(p.ctx_lens[s]), int(p.q_lens[s])
+        qs.append(wl.hash_normal_bf16(seed, wl.KIND_Q, rid, np.arange(c, c + n), [q_head], head_dim))
+        k = wl.hash_normal_bf16(seed, wl.KIND_K, rid, np.arange(0, c + n), [kv_head], head_dim)
+        v = wl.hash_normal_bf16(seed, wl.KIND_V, rid, np.arange(0, c + n), [kv_head], head_dim)
+        hk.append(k[:c]); kn.append(k[c:]); hv.append(v[:c]); vn.append(v[c:])
+    spec = wl.custom_spec("trace-sub", q_lens, ctx, 1, 1, head_dim, block_size, seed=1, slack=1.0)
+    tens = wl.PassTensors(q=np.concatenate(qs), k_new=np.concatenate(kn), v_new=np.concatenate(vn),
+                          hist_k=np.concatenate(hk), hist_v=np.concatenate(hv))
+    return oracle_pass(spec, tens)
