@@ -4,7 +4,8 @@
 // Kernels
 //   append_kernel   one work-group per (append run, kv head): copies the new K
 //                   rows into their block (slot-major) and writes the new V
-//                   rows transposed into the block's [D][B] layout through LDS.
+//                   rows transposed into the block's [D][B] layout (8x8 tiles
+//                   transposed in registers, 16-byte stores).
 //   attn_kernel     one work-group per work item.  Items with many query rows
 //                   (prompt-chunk tiles, GQA groups) take the matrix-core path:
 //                   K/V stages of 64 tokens staged in LDS, S^T = K Q^T and
@@ -486,13 +487,17 @@ __device__ void mfma_item(const AttnArgs& a, const ItemRec& it, uint16_t* lds) {
     if (active) {
       const uint16_t* kt = lds + (t & 1) * L::STAGE;
       const uint16_t* vt = kt + L::KT;
+      // S^T for both 32-token halves; consecutive MFMAs alternate between the
+      // two accumulators so no MFMA waits on the one just issued.
       f32x16 sacc[2];
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
+      for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
         for (int v = 0; v < 16; ++v) sacc[h2][v] = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
+      for (int kk = 0; kk < D / 16; ++kk) {
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
           const bf16x8 ka = __builtin_bit_cast(
               bf16x8, *reinterpret_cast<const u32x4*>(kt + (32 * h2 + l32) * L::KS + 16 * kk + 8 * hf));
           sacc[h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[kk], sacc[h2], 0, 0, 0);
@@ -553,12 +558,14 @@ __device__ void mfma_item(const AttnArgs& a, const ItemRec& it, uint16_t* lds) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) lrnd = dot2(w[e], kOnePair, lrnd);
         }
+      // O^T += V^T P^T; the dims loop is innermost so consecutive MFMAs use
+      // different accumulators.
 #pragma unroll
-      for (int dd = 0; dd < D / 32; ++dd)
+      for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
+          for (int dd = 0; dd < D / 32; ++dd) {
             const bf16x8 va = __builtin_bit_cast(
                 bf16x8, *reinterpret_cast<const u32x4*>(vt + (32 * dd + l32) * L::VS + 32 * h2 + 16 * ks + 8 * hf));
             o[dd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[h2][ks], o[dd], 0, 0, 0);
@@ -649,27 +656,74 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnArgs a, const Merge
   store_result(a, sq, it, D, r, PL * lane, acc, PL, lane == 0, mx + fast_log2(wsum) * kLn2);
 }
 
+// Append of one run (up to B consecutive new tokens of one sequence in one
+// block) for one kv head.  K rows are copied with 16-byte loads and stores.
+// V is written transposed: a thread takes an aligned group of 8 block slots
+// and 8 dims, loads the 8 token rows' 16-byte dim chunks, transposes the 8x8
+// bf16 tile in registers (v_perm_b32 picks 16-bit halves) and stores 8
+// contiguous 16-byte slot runs, one per dim; groups the run only partly covers
+// store their valid slots with 2-byte stores, so no byte outside the run is
+// written.
+__device__ __forceinline__ uint32_t pick_lo(uint32_t a, uint32_t b) {
+  // {a.lo, b.lo} as (low half, high half)
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pick_hi(uint32_t a, uint32_t b) {
+  // {a.hi, b.hi}
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
 template <int D, int B>
 __global__ __launch_bounds__(kThreads) void append_kernel(const RunRec* runs, const uint16_t* k_new,
                                                            const uint16_t* v_new, uint16_t* kpool,
                                                            uint16_t* vpool, int hkv) {
   constexpr int CPR = D / 8;
-  constexpr int VS = D + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t vtile[B * VS];
   const RunRec run = runs[blockIdx.x];
   const int g = blockIdx.y;
   uint16_t* kdst = kpool + ((size_t(run.block) * hkv + g) * B + run.slot0) * D;
   for (int c = threadIdx.x; c < run.count * CPR; c += kThreads) {
     const int i = c / CPR, dc = c % CPR;
-    const size_t src = (size_t(run.tok0 + i) * hkv + g) * D + 8 * dc;
-    st16(kdst + i * D + 8 * dc, ld16(k_new + src));
-    st16(vtile + i * VS + 8 * dc, ld16(v_new + src));
+    st16(kdst + i * D + 8 * dc, ld16(k_new + (size_t(run.tok0 + i) * hkv + g) * D + 8 * dc));
   }
-  __syncthreads();
-  uint16_t* vdst = vpool + (size_t(run.block) * hkv + g) * D * B + run.slot0;
-  for (int e = threadIdx.x; e < run.count * D; e += kThreads) {
-    const int d = e / run.count, i = e % run.count;
-    vdst[size_t(d) * B + i] = vtile[i * VS + d];
+  uint16_t* vblk = vpool + (size_t(run.block) * hkv + g) * D * B;
+  const int first = run.slot0 / 8;
+  const int groups = (run.slot0 + run.count - 1) / 8 - first + 1;
+  for (int e = threadIdx.x; e < groups * CPR; e += kThreads) {
+    const int cg = e % groups, dg = e / groups;   // slot group fastest: coalesced stores
+    const int s0 = 8 * (first + cg);
+    u32x4 r[8];
+    bool full = true;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = s0 + u - run.slot0;
+      const bool ok = i >= 0 && i < run.count;
+      full = full && ok;
+      r[u] = ok ? ld16(v_new + (size_t(run.tok0 + i) * hkv + g) * D + 8 * dg) : u32x4{0u, 0u, 0u, 0u};
+    }
+    // out[d] holds slots s0..s0+7 of dim 8*dg + d
+    u32x4 out[8];
+#pragma unroll
+    for (int w = 0; w < 4; ++w)          // word w of a row holds dims 2w, 2w+1
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {      // output word k holds slots 2k, 2k+1
+        out[2 * w][k] = pick_lo(r[2 * k][w], r[2 * k + 1][w]);
+        out[2 * w + 1][k] = pick_hi(r[2 * k][w], r[2 * k + 1][w]);
+      }
+    if (full) {
+#pragma unroll
+      for (int d = 0; d < 8; ++d) st16(vblk + size_t(8 * dg + d) * B + s0, out[d]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = s0 + u - run.slot0;
+        if (i < 0 || i >= run.count) continue;
+#pragma unroll
+        for (int d = 0; d < 8; ++d) {
+          const uint32_t w = out[d][u >> 1];
+          vblk[size_t(8 * dg + d) * B + s0 + u] = uint16_t((u & 1) ? (w >> 16) : (w & 0xffffu));
+        }
+      }
+    }
   }
 }
 

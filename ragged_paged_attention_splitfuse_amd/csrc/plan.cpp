@@ -43,11 +43,17 @@ constexpr double kItemsPerCu = 4.0;
 // Matrix-core tiles: relative cost per KV token of a tile with R padded rows
 // is max(kMfmaMinCost, R / kFlopPerByte), where kFlopPerByte is the ratio of
 // achievable bf16 MFMA rate to achievable HBM rate on MI355X (about
-// 1000 TFLOP/s : 6 TB/s).  A split of a tile also moves its partial rows
-// through the workspace, so tiles are not split below kMfmaMinSplitTokens.
+// 1000 TFLOP/s : 6 TB/s).  Splitting a prefill tile (two or more wavefronts)
+// buys no attention time once there are at least as many tiles as CUs, but
+// moves its partial rows through the workspace and adds the merge, so such
+// tiles are split only when they are too few to occupy the CUs (then to about
+// kMfmaSlotsPerCu items per CU, never below kMfmaMinSplitTokens).  One-wave
+// groups (GQA decodes) are bandwidth-bound like decodes and use the common
+// target.
 constexpr double kFlopPerByte = 170.0;
 constexpr double kMfmaMinCost = 0.5;
-constexpr int kMfmaMinSplitTokens = 512;
+constexpr int kMfmaMinSplitTokens = 1024;
+constexpr int kMfmaSlotsPerCu = 2;
 
 size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -185,6 +191,17 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
 
     // ---- split each group's visible range [0, vis_end)
     const double target = std::max(1.0, total_cost / (double(target_cus) * kItemsPerCu));
+    int64_t tile_groups = 0;
+    double tile_cost = 0.0;
+    for (const Group& grp : groups)
+      if (grp.waves >= 2) {
+        ++tile_groups;
+        tile_cost += grp.cost;
+      }
+    const double tile_target =
+        tile_groups >= target_cus
+            ? 1e300
+            : std::max(1.0, tile_cost / (double(target_cus) * kMfmaSlotsPerCu));
     std::vector<Pending> mfma, valu;
     std::vector<MergeRec> merges;
     int64_t partial_rows = 0;
@@ -196,9 +213,10 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
       if (d->force_splits > 0) {
         k = d->force_splits;
       } else {
-        k = int64_t(ceil(grp.cost / target));
+        k = int64_t(ceil(grp.cost / (grp.waves >= 2 ? tile_target : target)));
         k = std::min<int64_t>(k, max_splits);
-        const int floor_tokens = grp.waves ? std::max(min_split, kMfmaMinSplitTokens) : min_split;
+        const int floor_tokens =
+            grp.waves >= 2 ? std::max(min_split, kMfmaMinSplitTokens) : min_split;
         k = std::min<int64_t>(k, std::max<int64_t>(1, grp.vis_end / std::max(1, floor_tokens)));
       }
       k = std::max<int64_t>(1, std::min<int64_t>(k, ceil_div(grp.vis_end, fg::kKvTile)));
