@@ -132,8 +132,11 @@ fg_status fg_plan_pass(const fg_pass_desc* desc, fg_plan** out_plan);
 fg_status fg_plan_info(const fg_plan* plan, fg_plan_info_t* out);
 
 /* Copy the plan's metadata into d_meta (device, >= metadata_bytes,
- * caller-owned) with an asynchronous host-to-device copy on `stream`.  The
- * plan must stay alive until the stream has passed the copy. */
+ * caller-owned), asynchronously and in order on `stream`.  Plans up to 1 MiB
+ * are staged through a library-owned ring of pinned host buffers (allocated on
+ * first use, held until the process ends) and copied by a small kernel on the
+ * same stream; larger ones use hipMemcpyAsync, in which case the plan must stay
+ * alive until the stream has passed the copy. */
 fg_status fg_plan_upload(const fg_plan* plan, void* d_meta, void* stream);
 
 /* Scatter the pass's new K and V into their cache slots (asynchronous).

@@ -25,6 +25,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <string.h>
 
 #include <mutex>
 #include <vector>
@@ -770,6 +771,47 @@ struct ProfScope {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// ---------------------------------------------------------------- metadata upload
+// Plans are uploaded by a small kernel that reads a pinned host staging slot
+// over the host link and writes the device buffer, so the whole pass stays on
+// the caller's compute queue (a copy-engine transfer costs a cross-engine
+// hand-off before the next kernel).  A ring of kStageSlots pinned slots is
+// allocated on first use and held until the process ends; a slot is reused
+// only after the event recorded behind its last upload has completed.
+// Plans larger than a slot fall back to hipMemcpyAsync.
+constexpr int kStageSlots = 8;
+constexpr size_t kStageSlotBytes = size_t(1) << 20;
+
+struct StageSlot {
+  void* host = nullptr;
+  hipEvent_t done = nullptr;
+  bool pending = false;
+};
+std::mutex g_stage_mu;
+StageSlot g_stage[kStageSlots];
+int g_stage_next = 0;
+int g_stage_state = 0;  // 0 untried, 1 ready, -1 unavailable (fall back to copies)
+
+bool stage_ready() {
+  if (g_stage_state == 0) {
+    g_stage_state = 1;
+    for (StageSlot& slot : g_stage) {
+      if (hipHostMalloc(&slot.host, kStageSlotBytes, hipHostMallocDefault) != hipSuccess ||
+          hipEventCreateWithFlags(&slot.done, hipEventDisableTiming) != hipSuccess) {
+        g_stage_state = -1;
+        break;
+      }
+    }
+  }
+  return g_stage_state == 1;
+}
+
+__global__ __launch_bounds__(kThreads) void upload_kernel(const u32x4* __restrict__ src,
+                                                          u32x4* __restrict__ dst, unsigned n) {
+  const unsigned i = blockIdx.x * kThreads + threadIdx.x;
+  if (i < n) dst[i] = src[i];
+}
+
 #define FG_SWITCH_DB(D_, B_, MACRO)                 \
   do {                                              \
     if ((D_) == 64 && (B_) == 16) MACRO(64, 16);    \
@@ -795,8 +837,27 @@ extern "C" int fg_internal_device_cu_count(void) {
 
 extern "C" fg_status fg_plan_upload(const fg_plan* plan, void* d_meta, void* stream) {
   if (!plan || !d_meta || !aligned16(d_meta)) return FG_E_INVALID;
-  if (hipMemcpyAsync(d_meta, plan->blob.data(), plan->blob.size(), hipMemcpyHostToDevice,
-                     static_cast<hipStream_t>(stream)) != hipSuccess)
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t bytes = plan->blob.size();
+  std::lock_guard<std::mutex> lk(g_stage_mu);
+  if (bytes <= kStageSlotBytes && stage_ready()) {
+    StageSlot& slot = g_stage[g_stage_next];
+    g_stage_next = (g_stage_next + 1) % kStageSlots;
+    if (slot.pending) {
+      // the slot's previous upload was kStageSlots uploads ago; normally done
+      if (hipEventSynchronize(slot.done) != hipSuccess) return FG_E_HIP;
+      slot.pending = false;
+    }
+    memcpy(slot.host, plan->blob.data(), bytes);
+    const unsigned chunks = unsigned((bytes + 15) / 16);
+    hipLaunchKernelGGL(upload_kernel, dim3((chunks + kThreads - 1) / kThreads), dim3(kThreads), 0, s,
+                       reinterpret_cast<const u32x4*>(slot.host), static_cast<u32x4*>(d_meta), chunks);
+    if (hipGetLastError() != hipSuccess) return FG_E_HIP;
+    if (hipEventRecord(slot.done, s) != hipSuccess) return FG_E_HIP;
+    slot.pending = true;
+    return FG_OK;
+  }
+  if (hipMemcpyAsync(d_meta, plan->blob.data(), bytes, hipMemcpyHostToDevice, s) != hipSuccess)
     return FG_E_HIP;
   return FG_OK;
 }

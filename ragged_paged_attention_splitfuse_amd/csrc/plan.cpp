@@ -258,7 +258,7 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
       }
     }
 
-    // Longest first within each path (ties keep plan order: deterministic).
+    // Longest first within each kind (ties keep plan order: deterministic).
     auto longest_first = [](const Pending& a, const Pending& b) {
       if (a.cost != b.cost) return a.cost > b.cost;
       return a.order < b.order;
@@ -299,8 +299,19 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
     if (!bt.empty()) memcpy(base + plan->off_bt, bt.data(), sizeof(int32_t) * bt.size());
     if (!runs.empty()) memcpy(base + plan->off_runs, runs.data(), sizeof(RunRec) * runs.size());
     ItemRec* items = reinterpret_cast<ItemRec*>(base + plan->off_items);
-    for (size_t i = 0; i < mfma.size(); ++i) items[i] = mfma[i].item;
-    for (size_t i = 0; i < valu.size(); ++i) items[mfma.size() + i] = valu[i].item;
+    {
+      // Dispatch order: the two item kinds (compute-bound tiles, bandwidth-
+      // bound decode rows) are spread evenly over the order, each kind
+      // longest-first, so a CU holds a mix of both rather than a round of
+      // tiles followed by a round of decodes.
+      size_t a = 0, b = 0, o = 0;
+      const double na = double(mfma.size()), nb = double(valu.size());
+      while (a < mfma.size() || b < valu.size()) {
+        const bool take_a = b >= valu.size() ||
+                            (a < mfma.size() && (double(a) + 0.5) / na <= (double(b) + 0.5) / nb);
+        items[o++] = take_a ? mfma[a++].item : valu[b++].item;
+      }
+    }
     if (!merges.empty())
       memcpy(base + plan->off_merges, merges.data(), sizeof(MergeRec) * merges.size());
 
