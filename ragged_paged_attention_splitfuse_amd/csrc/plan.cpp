@@ -69,6 +69,59 @@ struct Pending {
   int32_t order;
 };
 
+// The first launch rounds are resident together: the matrix-core kernel
+// holds kMfmaSlotsPerCu work-groups per CU, and MI355X's dispatcher hands
+// work-group p of a fresh launch to CU (p mod C) in round p / C (it deals
+// them round-robin over the XCDs and, within each, one per CU before a
+// second).  Two work-groups on one CU share its matrix cores, so the CU
+// finishes with the sum of their costs.  Longest-first order would pair the
+// longest item with the (C+1)-th longest; instead the first C * kMfmaSlotsPerCu
+// items are dealt costliest-first onto the least-loaded CU with a free slot
+// (greedy multiway partition) and written back at positions cu + round * C,
+// CUs holding fewer items last.  Items after those rounds keep their order
+// and fill whichever CU frees a slot first.  Only speed depends on this.
+void place_resident_rounds(std::vector<Pending>& list, int cus) {
+  const size_t c = size_t(cus);
+  const size_t m = std::min(list.size(), c * kMfmaSlotsPerCu);
+  if (m <= c) return;
+  std::vector<size_t> idx(m);
+  std::iota(idx.begin(), idx.end(), size_t(0));
+  std::stable_sort(idx.begin(), idx.end(),
+                   [&](size_t x, size_t y) { return list[x].cost > list[y].cost; });
+  std::vector<double> load(c, 0.0);
+  std::vector<std::vector<size_t>> bins(c);
+  // (load, cu) min-heap over CUs with a free slot; ties go to the lower cu.
+  using Entry = std::pair<double, size_t>;
+  std::vector<Entry> heap;
+  for (size_t u = 0; u < c; ++u) heap.push_back({0.0, u});
+  auto cmp = [](const Entry& x, const Entry& y) {
+    return x.first != y.first ? x.first > y.first : x.second > y.second;
+  };
+  std::make_heap(heap.begin(), heap.end(), cmp);
+  for (size_t i : idx) {
+    std::pop_heap(heap.begin(), heap.end(), cmp);
+    Entry e = heap.back();
+    heap.pop_back();
+    bins[e.second].push_back(i);
+    e.first += list[i].cost;
+    if (bins[e.second].size() < size_t(kMfmaSlotsPerCu)) {
+      heap.push_back(e);
+      std::push_heap(heap.begin(), heap.end(), cmp);
+    }
+  }
+  // Fuller bins first: round r covers positions r*C .. r*C + (items in round) - 1.
+  std::stable_sort(bins.begin(), bins.end(),
+                   [](const std::vector<size_t>& x, const std::vector<size_t>& y) {
+                     return x.size() > y.size();
+                   });
+  std::vector<Pending> placed;
+  placed.reserve(m);
+  for (size_t r = 0; r < size_t(kMfmaSlotsPerCu); ++r)
+    for (size_t u = 0; u < c; ++u)
+      if (r < bins[u].size()) placed.push_back(list[bins[u][r]]);
+  std::copy(placed.begin(), placed.end(), list.begin());
+}
+
 fg_status validate(const fg_pass_desc* d) {
   if (d->num_seqs < 0) return FG_E_INVALID;
   if (d->num_q_heads < 1 || d->num_kv_heads < 1) return FG_E_INVALID;
@@ -304,13 +357,17 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
       // bound decode rows) are spread evenly over the order, each kind
       // longest-first, so a CU holds a mix of both rather than a round of
       // tiles followed by a round of decodes.
-      size_t a = 0, b = 0, o = 0;
+      std::vector<Pending> order_list;
+      order_list.reserve(mfma.size() + valu.size());
+      size_t a = 0, b = 0;
       const double na = double(mfma.size()), nb = double(valu.size());
       while (a < mfma.size() || b < valu.size()) {
         const bool take_a = b >= valu.size() ||
                             (a < mfma.size() && (double(a) + 0.5) / na <= (double(b) + 0.5) / nb);
-        items[o++] = take_a ? mfma[a++].item : valu[b++].item;
+        order_list.push_back(take_a ? mfma[a++] : valu[b++]);
       }
+      if (!mfma.empty()) place_resident_rounds(order_list, target_cus);
+      for (size_t o = 0; o < order_list.size(); ++o) items[o] = order_list[o].item;
     }
     if (!merges.empty())
       memcpy(base + plan->off_merges, merges.data(), sizeof(MergeRec) * merges.size());

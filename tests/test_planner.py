@@ -65,18 +65,42 @@ def test_long_decodes_are_split_short_ones_not():
     assert per_seq[1:].max() == 32     # one item per head, no split
 
 
+def _item_costs(items):
+    lengths = (items[:, 5] - items[:, 4]).astype(np.float64)
+    mf = items[:, 7] > 0
+    # matrix-core cost per token grows with the tile's wavefront count
+    return np.where(mf, lengths * np.maximum(0.5, items[:, 7] * 32 / 170.0), lengths), mf
+
+
 def test_items_are_longest_first_per_kind_and_interleaved():
     for name in ("7b_decode64", "7b_pass2048", "70b_share4096"):
         items = plan_of(wl.config_spec(name)).metadata()["items"]
-        lengths = (items[:, 5] - items[:, 4]).astype(np.int64)
-        mf = items[:, 7] > 0
-        # matrix-core cost per token grows with the tile's wavefront count
-        cost = lengths[mf] * np.maximum(0.5, items[mf, 7] * 32 / 170.0)
-        assert np.all(np.diff(cost) <= 1e-9) and np.all(np.diff(lengths[~mf]) <= 0)
+        cost, mf = _item_costs(items)
+        # with tiles present, the two resident rounds are reordered for balance
+        m = min(len(items), 2 * CUS) if mf.any() else 0
+        cost, mf = cost[m:], mf[m:]
+        assert np.all(np.diff(cost[mf]) <= 1e-9) and np.all(np.diff(cost[~mf]) <= 0)
         if mf.any() and (~mf).any():
             # both kinds spread over the whole order
-            pos = np.nonzero(mf)[0] / len(items)
+            pos = np.nonzero(mf)[0] / len(cost)
             assert pos.min() < 0.05 and pos.max() > 0.95
+
+
+@pytest.mark.parametrize("name", ["7b_chunk2032", "70b_chunks", "70b_share4096", "7b_pass2048"])
+def test_resident_rounds_balance_cu_pairs(name):
+    # positions p and p + CUS share a CU; their summed cost is evened out
+    items = plan_of(wl.config_spec(name)).metadata()["items"]
+    cost, _ = _item_costs(items)
+    m = min(len(items), 2 * CUS)
+    loads = cost[:CUS].copy()
+    loads[:m - CUS] += cost[CUS:m]
+    top = np.sort(cost[:m])[::-1]            # the same items, paired in sorted order
+    naive = top[:CUS].copy()
+    naive[:m - CUS] += top[CUS:m]
+    assert loads.max() <= naive.max() + 1e-9
+    assert loads.max() - loads.min() <= cost[:m].max() + 1e-9
+    if name in ("7b_chunk2032", "70b_chunks"):
+        assert loads.max() <= 1.01 * loads.mean()
 
 
 def test_tiny_plan_has_no_splits_and_no_workspace():
