@@ -27,7 +27,10 @@ sys.path.insert(0, ROOT)
 METRIC = "µs per SplitFuse attention pass + KV GB/s & MFMA TFLOP/s as % of peak, 7B shape"
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
-KERNEL_SOURCE = os.path.join(ROOT, "ragged_paged_attention_splitfuse_amd", "csrc", "fg_device.hip")
+# Sources that decide what the attention kernel reads and writes: the kernels
+# themselves and the planner that cuts the work items.
+KERNEL_SOURCES = [os.path.join(ROOT, "ragged_paged_attention_splitfuse_amd", "csrc", f)
+                  for f in ("fg_device.hip", "plan.cpp", "plan.h", "fg_meta.h")]
 
 
 def algorithmic(spec, out_bytes=4):
@@ -46,8 +49,101 @@ def algorithmic(spec, out_bytes=4):
 
 
 def source_hash():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def achievable_peaks(torch, dev, stream, copy_mib=1024, gemm_n=8192, iters=10):
+    """Achievable rates measured in the same run: a device-to-device copy (HBM
+    read + write) and a bf16 GEMM through the vendor BLAS (matrix cores)."""
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(iters):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / iters
+    n = copy_mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: dst.copy_(src))
+    del src, dst
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    a = torch.randn((gemm_n, gemm_n), dtype=torch.bfloat16, device=dev, generator=g)
+    b = torch.randn((gemm_n, gemm_n), dtype=torch.bfloat16, device=dev, generator=g)
+    t_gemm = timed(lambda: torch.mm(a, b))
+    del a, b
+    return {"copy_gbs": round(2 * n / t_copy / 1e9, 1), "copy_bytes": n,
+            "bf16_gemm_tflops": round(2 * gemm_n ** 3 / t_gemm / 1e12, 1),
+            "gemm_shape": [gemm_n, gemm_n, gemm_n]}
+
+
+def _pmc_per_dispatch(run_dir, counter):
+    """{kernel name: [value per dispatch]} from one rocprofv3 --pmc csv run."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {run_dir}")
+    per = {}
+    for path in files:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = (r["Kernel_Name"], path, int(r["Dispatch_Id"]))
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])   # sum over dimensions
+    out = {}
+    for (name, _, _), v in per.items():
+        out.setdefault(name, []).append(v)
+    return out
+
+
+def write_traffic(workload, fetch_dir, write_dir, probe_mib):
+    """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE,
+    both with --copy-probe-mib) into profiles/traffic_<workload>.json.
+
+    Each counter is read in KiB per dispatch and scaled by what it reads for the
+    plain device-to-device copy of probe_mib MiB in the same run (that copy
+    reads and writes exactly probe_mib MiB)."""
+    probe = probe_mib << 20
+    flag = "" if workload == "7b_pass2048" else f" --workload {workload}"
+    rec = {"workload": workload, "kernel_source_sha256_16": source_hash(),
+           "copy_probe_bytes": probe,
+           "commands": [f"rocprofv3 --pmc {c} -d {d} -o pmc --output-format csv -- python bench.py "
+                        f"--no-cpu --no-achievable{flag} --steps 5 --warmup 1 --cold-iters 0 "
+                        f"--copy-probe-mib {probe_mib}"
+                        for c, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir))] +
+                       [f"python bench.py{flag} --traffic-from {fetch_dir} {write_dir} "
+                        f"--copy-probe-mib {probe_mib}"]}
+    total = 0.0
+    for counter, run_dir in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        vals = _pmc_per_dispatch(run_dir, counter)
+        copies = [v for n, vs in vals.items() if "copyBuffer" in n or "copy_kernel" in n for v in vs]
+        attn = [v for n, vs in vals.items() if "attn_kernel" in n for v in vs]
+        if not copies or not attn:
+            raise SystemExit(f"{counter}: copy probe or attn_kernel dispatches missing in {run_dir}")
+        factor = max(copies) * 1024.0 / probe
+        per_launch = sum(attn) / len(attn) * 1024.0 / factor
+        key = "fetch" if counter == "FETCH_SIZE" else "write"
+        rec[f"{key}_counter_factor"] = round(factor, 4)
+        rec[f"{key}_kib_per_launch_raw"] = round(sum(attn) / len(attn), 1)
+        rec[f"attn_{key}_bytes_per_launch"] = int(per_launch)
+        rec[f"{key}_dispatches"] = len(attn)
+        total += per_launch
+    rec["attn_hbm_bytes_per_launch"] = int(total)
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
 
 
 def load_traffic(workload):
@@ -217,7 +313,18 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (a known-size "
                          "kernel that calibrates HBM byte counters)")
+    ap.add_argument("--no-achievable", action="store_true",
+                    help="skip the achievable-peak probes (copy and bf16 GEMM)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU run: write profiles/traffic_<workload>.json from two "
+                         "rocprofv3 --pmc output folders of this script (FETCH_SIZE, "
+                         "WRITE_SIZE) taken with --copy-probe-mib")
     args = ap.parse_args()
+    if args.traffic_from:
+        if args.copy_probe_mib <= 0:
+            raise SystemExit("--traffic-from needs the --copy-probe-mib the runs used")
+        write_traffic(args.workload, args.traffic_from[0], args.traffic_from[1], args.copy_probe_mib)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this path runs on one GPU only; multi-GPU runs are not "
@@ -333,6 +440,11 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
+    achievable = None if args.no_achievable else achievable_peaks(torch, dev, stream)
+    if achievable:
+        ach = achievable["copy_gbs"] if bound == "hbm" else achievable["bf16_gemm_tflops"]
+        roof["achievable_peak"] = ach
+        roof["frac_of_achievable"] = round(roof["achieved"] / ach, 4)
     roof["kernel"] = "attn_kernel"
     roof["algorithmic_per_launch"] = alg["attn_bytes"] if bound == "hbm" else alg["flops"]
 
@@ -375,6 +487,10 @@ def main():
             "plan": {k: info[k] for k in ("num_items", "num_valu_items", "num_mfma_items",
                                           "num_merge_groups", "max_splits_used", "target_cus")},
             "algorithmic": alg,
+            "achievable": achievable,
+            "attn_frac_of_achievable": {
+                "hbm": round(attn_gbs / achievable["copy_gbs"], 4),
+                "mfma": round(attn_tflops / achievable["bf16_gemm_tflops"], 4)} if achievable else None,
             "kernel_source_sha256_16": source_hash(),
         },
     }
