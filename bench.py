@@ -299,6 +299,127 @@ def run_trace(args, torch, fgb, wl):
     print(json.dumps(res), flush=True)
 
 
+def knobs_of(args, fgb):
+    policy = {"balanced": fgb.FG_SPLIT_BALANCED, "engine": fgb.FG_SPLIT_ENGINE,
+              "per1k": fgb.FG_SPLIT_PER_1K}[args.split_policy]
+    return {"target_cus": args.target_cus, "split_policy": policy, "force_splits": args.force_splits}
+
+
+def measure_pass(torch, fgb, spec, tens, dev, stream, knobs, steps, warmup):
+    """Set up pools and inputs of one pass, then time `steps` passes (plan,
+    upload, append, attention) back to back after `warmup` untimed ones.
+    Per-kernel times come from the library's HIP events on the launch stream."""
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    kshape, vshape = fgb.pool_shapes(spec.num_blocks, spec.num_kv_heads, spec.block_size, spec.head_dim)
+    kp = torch.zeros(kshape, dtype=torch.bfloat16, device=dev)
+    vp = torch.zeros(vshape, dtype=torch.bfloat16, device=dev)
+    hist = spec.history_pass()
+    if hist is not None:
+        hplan = fgb.Plan(hist[0], hist[1], hist[2], spec.num_q_heads, spec.num_kv_heads,
+                         spec.head_dim, spec.block_size, spec.num_blocks)
+        fgb.kv_append(hplan, hplan.upload(), to_dev(tens.hist_k), to_dev(tens.hist_v), kp, vp)
+        torch.cuda.synchronize()
+        hplan.close()
+    q, kn, vn = to_dev(tens.q), to_dev(tens.k_new), to_dev(tens.v_new)
+    t, hq, d = spec.num_tokens, spec.num_q_heads, spec.head_dim
+    out = torch.empty((t, hq, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((t, hq), dtype=torch.float32, device=dev)
+
+    probe = fgb.Plan.from_spec(spec, **knobs)
+    info = probe.info
+    meta = torch.empty(max(16, info["metadata_bytes"]), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(16, info["workspace_bytes"]), dtype=torch.uint8, device=dev)
+    probe.close()
+
+    host_plan_s = []
+
+    def step(keep):
+        h0 = time.perf_counter()
+        plan = fgb.Plan.from_spec(spec, **knobs)
+        host_plan_s.append(time.perf_counter() - h0)
+        plan.upload(meta, stream)
+        fgb.kv_append(plan, meta, kn, vn, kp, vp, stream)
+        fgb.attention_ragged(plan, meta, q, kp, vp, out, lse, workspace=ws, stream=stream)
+        keep.append(plan)
+
+    keep = []
+    for _ in range(warmup):
+        step(keep)
+    torch.cuda.synchronize()
+    keep.clear()
+    host_plan_s.clear()
+
+    fgb.fg_profile_read()
+    fgb.fg_profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(keep)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    fgb.fg_profile_enable(False)
+    kern = fgb.fg_profile_read()
+    keep.clear()
+    return {"step": step, "keep": keep, "kern": kern, "info": info, "host_plan_s": host_plan_s,
+            "ms_per_step": (t1 - t0) * 1e3 / steps}
+
+
+def kernel_us(kern):
+    out = {}
+    for key, name in (("append", "append_kernel"), ("attention", "attn_kernel"), ("merge", "merge_kernel")):
+        ms, n = kern[name]
+        out[key] = ms * 1e3 / n if n else 0.0
+    return out
+
+
+SWEEP_BUDGETS = (256, 512, 1024, 2048, 4096, 8192)
+
+
+def run_sweep(args, torch, fgb, wl, dev, stream, knobs):
+    """Token-budget sweep of the fused pass: the cfg-2 mix (16 decodes plus one
+    prompt chunk filling the budget) at budgets 256 .. 8192 tokens."""
+    rows = []
+    for budget in SWEEP_BUDGETS:
+        spec = wl.config_spec(f"7b_budget{budget}")
+        tens = wl.make_tensors(spec)
+        alg = algorithmic(spec)
+        m = measure_pass(torch, fgb, spec, tens, dev, stream, knobs, args.steps, args.warmup)
+        ku = kernel_us(m["kern"])
+        pass_us = m["ms_per_step"] * 1e3
+        rows.append({"budget": budget, "pass_us": round(pass_us, 2),
+                     "tokens_per_s": round(budget / (pass_us * 1e-6), 1),
+                     "kernel_us": {k: round(v, 2) for k, v in ku.items()},
+                     "attn_tflops": round(alg["flops"] / (ku["attention"] * 1e-6) / 1e12, 1),
+                     "attn_gbs": round(alg["attn_bytes"] / (ku["attention"] * 1e-6) / 1e9, 1),
+                     "chunk_ctx": int(spec.ctx_lens[-1]), "items": m["info"]["num_items"]})
+        print(json.dumps({"budget": budget, "pass_us": rows[-1]["pass_us"]}), file=sys.stderr, flush=True)
+        del m, tens
+        torch.cuda.empty_cache()
+    tps = np.array([r["tokens_per_s"] for r in rows])
+    knee = next(r["budget"] for r, v in zip(rows, tps) if v >= 0.9 * tps.max())
+    # latency against tokens: least-squares line through (budget, pass µs)
+    bud = np.array([r["budget"] for r in rows], dtype=np.float64)
+    lat = np.array([r["pass_us"] for r in rows])
+    slope, icpt = np.polyfit(bud, lat, 1)
+    gain = np.diff(tps) / np.diff(np.log2(bud))   # throughput gained per doubling
+    res = {
+        "metric": "token-budget sweep of the fused SplitFuse pass (7B shape, 16 decodes + chunk)",
+        "value": float(tps.max()), "unit": "tokens/s (max over budgets)", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "sweep", "budgets": list(SWEEP_BUDGETS)},
+        "roofline": None, "cpu_baseline": None,
+        "detail": {"points": rows, "knee_budget_90pct": knee,
+                   "latency_fit_us": {"per_token": round(float(slope), 5),
+                                      "intercept": round(float(icpt), 2)},
+                   "throughput_gain_per_doubling": [round(float(x), 1) for x in gain],
+                   "throughput_concave": bool(np.all(np.diff(gain) <= 0))},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -313,6 +434,10 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (a known-size "
                          "kernel that calibrates HBM byte counters)")
+    ap.add_argument("--split-policy", choices=["balanced", "engine", "per1k"], default="balanced",
+                    help="planner split-count policy (speed only; results are identical)")
+    ap.add_argument("--force-splits", type=int, default=0,
+                    help="static split count for every row group (FlashDecoding-style)")
     ap.add_argument("--no-achievable", action="store_true",
                     help="skip the achievable-peak probes (copy and bf16 GEMM)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -347,65 +472,17 @@ def main():
     if args.workload == "trace512":
         run_trace(args, torch, fgb, wl)
         return
+    if args.workload == "sweep":
+        run_sweep(args, torch, fgb, wl, dev, stream, knobs_of(args, fgb))
+        return
     spec = wl.config_spec(args.workload)
     tens = wl.make_tensors(spec)
     alg = algorithmic(spec)
-
-    def to_dev(bits):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
-
-    kshape, vshape = fgb.pool_shapes(spec.num_blocks, spec.num_kv_heads, spec.block_size, spec.head_dim)
-    kp = torch.zeros(kshape, dtype=torch.bfloat16, device=dev)
-    vp = torch.zeros(vshape, dtype=torch.bfloat16, device=dev)
-    hist = spec.history_pass()
-    if hist is not None:
-        hplan = fgb.Plan(hist[0], hist[1], hist[2], spec.num_q_heads, spec.num_kv_heads,
-                         spec.head_dim, spec.block_size, spec.num_blocks)
-        fgb.kv_append(hplan, hplan.upload(), to_dev(tens.hist_k), to_dev(tens.hist_v), kp, vp)
-        torch.cuda.synchronize()
-        hplan.close()
-    q, kn, vn = to_dev(tens.q), to_dev(tens.k_new), to_dev(tens.v_new)
     t, hq, d = spec.num_tokens, spec.num_q_heads, spec.head_dim
-    out = torch.empty((t, hq, d), dtype=torch.float32, device=dev)
-    lse = torch.empty((t, hq), dtype=torch.float32, device=dev)
-
-    knobs = {"target_cus": args.target_cus}
-    probe = fgb.Plan.from_spec(spec, **knobs)
-    info = probe.info
-    meta = torch.empty(max(16, info["metadata_bytes"]), dtype=torch.uint8, device=dev)
-    ws = torch.empty(max(16, info["workspace_bytes"]), dtype=torch.uint8, device=dev)
-    probe.close()
-
-    host_plan_s = []
-
-    def step(keep):
-        h0 = time.perf_counter()
-        plan = fgb.Plan.from_spec(spec, **knobs)
-        host_plan_s.append(time.perf_counter() - h0)
-        plan.upload(meta, stream)
-        fgb.kv_append(plan, meta, kn, vn, kp, vp, stream)
-        fgb.attention_ragged(plan, meta, q, kp, vp, out, lse, workspace=ws, stream=stream)
-        keep.append(plan)
-
-    keep = []
-    for _ in range(args.warmup):
-        step(keep)
-    torch.cuda.synchronize()
-    keep.clear()
-    host_plan_s.clear()
-
-    fgb.fg_profile_read()
-    fgb.fg_profile_enable(True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(keep)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    fgb.fg_profile_enable(False)
-    kern = fgb.fg_profile_read()
-    keep.clear()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    knobs = knobs_of(args, fgb)
+    m = measure_pass(torch, fgb, spec, tens, dev, stream, knobs, args.steps, args.warmup)
+    step, keep, kern, info = m["step"], m["keep"], m["kern"], m["info"]
+    host_plan_s, ms_per_step = m["host_plan_s"], m["ms_per_step"]
 
     # cold-cache passes: 1 GiB written between passes evicts L2 and the 256 MB MALL
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -467,6 +544,7 @@ def main():
             "kv_tokens": alg["kv_tokens"], "decodes": int(np.sum(spec.q_lens == 1)),
             "chunk_tokens": [int(x) for x in spec.q_lens[spec.q_lens > 1]],
             "chunk_ctx": [int(x) for x in spec.ctx_lens[spec.q_lens > 1]],
+            "split_policy": args.split_policy if args.force_splits == 0 else f"static{args.force_splits}",
         },
         "roofline": roof,
         "cpu_baseline": None,

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define FG_ABI_VERSION 1
+#define FG_ABI_VERSION 2
 
 typedef int32_t fg_status;
 
@@ -103,8 +103,31 @@ typedef struct fg_pass_desc {
   int32_t min_split_tokens;   /* smallest KV range worth its own work item */
   int32_t max_splits;         /* cap on KV splits of one row group (<= 256) */
   int32_t force_splits;       /* > 0: split every row group's KV range into this
-                                 many parts regardless of cost (tests) */
+                                 many parts regardless of cost (tests, and the
+                                 static FlashDecoding-style policy) */
+  int32_t split_policy;       /* FG_SPLIT_*: how KV split counts are chosen when
+                                 force_splits is 0 */
 } fg_pass_desc;
+
+/* Split-count policies.  All give the same attention results; only speed
+ * differs.
+ *   FG_SPLIT_BALANCED  (default) per row group, from a cost model in KV tokens
+ *                      balanced over target_cus compute units.
+ *   FG_SPLIT_ENGINE    per sequence, the allocation engine of "DeepSpeed-FastGen
+ *                      Guide: Dynamic SplitKV Serving", section "Step 2: Dynamic
+ *                      SplitKV Allocation Engine": no split at or below
+ *                      min_split_tokens (default 256), else kv_len /
+ *                      min_split_tokens capped at 16, then every count scaled by
+ *                      target_cus / total when the total is smaller, and all
+ *                      ones when there are at least target_cus sequences.
+ *   FG_SPLIT_PER_1K    per sequence, kv_len / 1024 clamped to [1, 16]: the
+ *                      reading of the same page's figure "Dynamic SplitKV
+ *                      Two-Phase Attention Kernel Workflow" (512, 4096 and 16384
+ *                      tokens get 1, 4 and 16 splits).
+ * A sequence's count applies to each of its row groups.  Every count is then
+ * capped by max_splits and by the 64-token alignment of split ranges (a range
+ * of L tokens split k ways uses parts of ceil(ceil(L / k) / 64) * 64 tokens). */
+enum { FG_SPLIT_BALANCED = 0, FG_SPLIT_ENGINE = 1, FG_SPLIT_PER_1K = 2 };
 
 typedef struct fg_plan fg_plan;
 

@@ -21,6 +21,7 @@ FG_OK = 0
 FG_E_INVALID, FG_E_RANGE, FG_E_ALIAS, FG_E_UNSUPPORTED = -1, -2, -3, -4
 FG_E_WORKSPACE, FG_E_HIP, FG_E_NOMEM = -5, -6, -7
 FG_DTYPE_F32, FG_DTYPE_BF16 = 0, 1
+FG_SPLIT_BALANCED, FG_SPLIT_ENGINE, FG_SPLIT_PER_1K = 0, 1, 2
 FG_KERNEL_APPEND, FG_KERNEL_ATTENTION, FG_KERNEL_MERGE, FG_KERNEL_COUNT = 0, 1, 2, 3
 
 _I32P = ctypes.POINTER(ctypes.c_int32)
@@ -41,6 +42,7 @@ class fg_pass_desc(ctypes.Structure):
         ("q_lens", _I32P), ("ctx_lens", _I32P), ("block_tables", _I32P),
         ("target_cus", ctypes.c_int32), ("min_split_tokens", ctypes.c_int32),
         ("max_splits", ctypes.c_int32), ("force_splits", ctypes.c_int32),
+        ("split_policy", ctypes.c_int32),
     ]
 
 
@@ -139,7 +141,7 @@ class Plan:
 
     def __init__(self, q_lens, ctx_lens, block_tables, num_q_heads, num_kv_heads, head_dim,
                  block_size, num_blocks, scale=0.0, target_cus=0, min_split_tokens=0,
-                 max_splits=0, force_splits=0):
+                 max_splits=0, force_splits=0, split_policy=0):
         self._h = None
         q = np.ascontiguousarray(q_lens, dtype=np.int32)
         c = np.ascontiguousarray(ctx_lens, dtype=np.int32)
@@ -160,6 +162,7 @@ class Plan:
         d.block_tables = bt.ctypes.data_as(_I32P)
         d.target_cus, d.min_split_tokens = target_cus, min_split_tokens
         d.max_splits, d.force_splits = max_splits, force_splits
+        d.split_policy = split_policy
         h = ctypes.c_void_p()
         _check(lib().fg_plan_pass(ctypes.byref(d), ctypes.byref(h)), "fg_plan_pass")
         self._h = h

@@ -36,10 +36,12 @@ constexpr int64_t kMaxKvLen = int64_t(1) << 28;
 constexpr int kDefaultMinSplitTokens = 256;
 constexpr int kDefaultMaxSplits = 64;
 constexpr int kMaxSplitsLimit = 256;
-// Work items each CU should receive at least: items longer than
-// total / (CUs * kItemsPerCu) are split, so longest-first dispatch ends with
-// every CU busy until close to the mean.
-constexpr double kItemsPerCu = 4.0;
+// Items longer than total / (CUs * kItemsPerCu) are split.  Two per CU (one
+// per resident work-group slot) is enough for longest-first dispatch to end
+// with every CU busy until close to the mean; a finer target buys little
+// balance and costs partial-row traffic plus a merge launch (measured on the
+// 7B 2048-token pass: 256 us per pass at 2, 280 us at 3 and 4).
+constexpr double kItemsPerCu = 2.0;
 // Matrix-core tiles: relative cost per KV token of a tile with R padded rows
 // is max(kMfmaMinCost, R / kFlopPerByte), where kFlopPerByte is the ratio of
 // achievable bf16 MFMA rate to achievable HBM rate on MI355X (about
@@ -133,6 +135,7 @@ fg_status validate(const fg_pass_desc* d) {
   if (d->target_cus < 0 || d->min_split_tokens < 0) return FG_E_INVALID;
   if (d->max_splits < 0 || d->max_splits > kMaxSplitsLimit) return FG_E_INVALID;
   if (d->force_splits < 0 || d->force_splits > kMaxSplitsLimit) return FG_E_INVALID;
+  if (d->split_policy < FG_SPLIT_BALANCED || d->split_policy > FG_SPLIT_PER_1K) return FG_E_INVALID;
   if (d->num_seqs > 0 && (!d->q_lens || !d->ctx_lens || !d->block_tables)) return FG_E_INVALID;
   return FG_OK;
 }
@@ -242,6 +245,28 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
       }
     }
 
+    // ---- per-sequence split counts of the pages' policies (FG_SPLIT_ENGINE,
+    // FG_SPLIT_PER_1K; see fg.h), from each sequence's KV length
+    std::vector<int64_t> seq_splits(size_t(S), 1);
+    if (d->split_policy == FG_SPLIT_ENGINE && S > 0) {
+      const int64_t chunk_min = d->min_split_tokens > 0 ? d->min_split_tokens : kDefaultMinSplitTokens;
+      if (S < target_cus) {
+        int64_t total = 0;
+        for (int s = 0; s < S; ++s) {
+          const int64_t len = seqs[s].kv_len;
+          seq_splits[size_t(s)] = len <= chunk_min ? 1 : std::min<int64_t>(std::max<int64_t>(1, len / chunk_min), 16);
+          total += seq_splits[size_t(s)];
+        }
+        if (total < target_cus) {
+          const double factor = double(target_cus) / double(total);
+          for (int64_t& k : seq_splits) k = std::max<int64_t>(1, int64_t(double(k) * factor));
+        }
+      }
+    } else if (d->split_policy == FG_SPLIT_PER_1K) {
+      for (int s = 0; s < S; ++s)
+        seq_splits[size_t(s)] = std::min<int64_t>(std::max<int64_t>(1, seqs[s].kv_len / 1024), 16);
+    }
+
     // ---- split each group's visible range [0, vis_end)
     const double target = std::max(1.0, total_cost / (double(target_cus) * kItemsPerCu));
     int64_t tile_groups = 0;
@@ -265,6 +290,8 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
       int64_t k;
       if (d->force_splits > 0) {
         k = d->force_splits;
+      } else if (d->split_policy != FG_SPLIT_BALANCED) {
+        k = std::min<int64_t>(seq_splits[size_t(grp.seq)], max_splits);
       } else {
         k = int64_t(ceil(grp.cost / (grp.waves >= 2 ? tile_target : target)));
         k = std::min<int64_t>(k, max_splits);

@@ -199,9 +199,22 @@ def config_spec(cfg, seed=None):
       3 / "7b_decode64"    64 decodes, ctx log-uniform 512..16000, 7B shape
       4 / "70b_share4096"  32 decodes + two 2032-token chunks, 16 q / 2 kv heads
       "70b_decode32", "70b_chunks"  its two halves
+      "7b_budget<N>"       token-budget sweep point: the 16 decodes of cfg 2 plus
+                           one prompt chunk of N - 16 tokens, the final chunk of
+                           cfg 2's prompt P (context max(0, P - (N - 16)))
     """
     names = {1: "tiny", 2: "7b_pass2048", 3: "7b_decode64", 4: "70b_share4096"}
     name = names.get(cfg, cfg)
+    if isinstance(name, str) and name.startswith("7b_budget"):
+        budget = int(name[len("7b_budget"):])
+        if budget < 32:
+            raise ValueError("budget must be at least 32 tokens")
+        rng = np.random.Generator(np.random.PCG64(2 if seed is None else seed))
+        dec = _decode_ctx(rng, 16)
+        prompt = int(_chunk_ctx(rng, 1, 2032)[0]) + 2032
+        n = budget - 16
+        return custom_spec(name, [1] * 16 + [n], list(dec) + [max(0, prompt - n)],
+                           32, 32, 128, 64, 2 if seed is None else seed, rng=rng)
     base = {"tiny": 1, "7b_pass2048": 2, "7b_decode16": 2, "7b_chunk2032": 2,
             "7b_decode64": 3, "70b_share4096": 4, "70b_decode32": 4, "70b_chunks": 4}
     if name not in base:

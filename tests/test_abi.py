@@ -3,6 +3,8 @@ import ctypes
 import os
 import re
 
+import pytest
+
 from ragged_paged_attention_splitfuse_amd import binding
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "fg.h")
@@ -33,13 +35,35 @@ def test_binding_covers_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert binding.fg_abi_version() == 1
+    assert binding.fg_abi_version() == 2
     assert binding.status_string(0) == "ok"
     assert "twice" in binding.status_string(binding.FG_E_ALIAS)
     assert binding.status_string(12345) == "unknown status"
 
 
-def test_struct_sizes_match_header_layout():
-    # fg_pass_desc: 7 int32 + float, 3 pointers, 4 int32; fg_plan_info_t: 3 int64 + 8 int32
-    assert ctypes.sizeof(binding.fg_pass_desc) == 32 + 24 + 16
-    assert ctypes.sizeof(binding.fg_plan_info_t) == 24 + 32
+def test_struct_sizes_match_header_layout(tmp_path):
+    """ctypes mirrors of the public structs agree with a C compiler's layout of
+    include/fg.h, field by field."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    structs = {"fg_pass_desc": binding.fg_pass_desc, "fg_plan_info_t": binding.fg_plan_info_t}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "fg.h"', "int main(void) {"]
+    for name, cls in structs.items():
+        lines.append(f'  printf("{name} %zu\\n", sizeof({name}));')
+        for field, _ in cls._fields_:
+            lines.append(f'  printf("{name}.{field} %zu\\n", offsetof({name}, {field}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run([cc, "-std=c99", "-I", inc, str(src), "-o", str(exe)], check=True)
+    got = dict(line.split() for line in subprocess.run([str(exe)], check=True, capture_output=True,
+                                                        text=True).stdout.splitlines())
+    for name, cls in structs.items():
+        assert int(got[name]) == ctypes.sizeof(cls), name
+        for field, _ in cls._fields_:
+            assert int(got[f"{name}.{field}"]) == getattr(cls, field).offset, (name, field)

@@ -96,6 +96,17 @@ def test_forced_split_counts(k):
     assert do <= SPLIT_O_TOL and dl <= LSE_TOL
 
 
+@pytest.mark.parametrize("policy", [fgb.FG_SPLIT_ENGINE, fgb.FG_SPLIT_PER_1K])
+def test_page_split_policies(policy):
+    # the pages' split policies only move work around: results stay on the oracle
+    spec = SMALL_SPECS["mha_d128_b64_mixed"]()
+    _log(f"[case] split policy {policy}")
+    tens, _, _, out, lse, plan = G.full_gpu_pass(spec, split_policy=policy, target_cus=16)
+    check_plan(plan, spec)
+    o_ref, l_ref = G.oracle_pass(spec, tens)
+    compare(out, lse, o_ref, l_ref, f"split_policy={policy}")
+
+
 def test_forced_splits_gqa_tiles():
     spec = SMALL_SPECS["gqa8_d128_b64_mixed"]()
     tens, _, _, out, lse, plan = G.full_gpu_pass(spec, force_splits=5)

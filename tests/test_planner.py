@@ -138,6 +138,8 @@ def test_validation_errors():
     _expect(fgb.FG_E_INVALID, scale=-1.0)
     _expect(fgb.FG_E_INVALID, force_splits=1000)
     _expect(fgb.FG_E_INVALID, target_cus=-3)
+    _expect(fgb.FG_E_INVALID, split_policy=3)
+    _expect(fgb.FG_E_INVALID, split_policy=-1)
 
 
 def test_unused_table_entries_are_ignored():
@@ -146,3 +148,57 @@ def test_unused_table_entries_are_ignored():
     assert plan.info["num_tokens"] == 4
     plan = fgb.Plan([3, 1], [0, 5], [[0, 1], [1, 2]], 4, 2, 128, 16, 4, target_cus=CUS)
     assert plan.info["num_tokens"] == 4
+
+
+# ---- the pages' split policies, native in the planner, against the oracle's
+# restatements (which the golden files pin)
+from oracle.split_policy import figure_rule, host_heuristic  # noqa: E402
+
+
+def _aligned(k, length):
+    """Parts a range of `length` tokens gets when asked for k splits of
+    64-token-aligned size (the planner's own alignment step)."""
+    k = max(1, min(k, -(-length // 64)))
+    chunk = -(-(-(-length // k)) // 64) * 64
+    return -(-length // chunk)
+
+
+def _splits_per_seq(plan, num_seqs):
+    items = plan.metadata()["items"]
+    items = items[items[:, 3] > 0]
+    out = []
+    for s in range(num_seqs):
+        sel = items[items[:, 0] == s]
+        # one kv head suffices: every head of a sequence gets the same count
+        sel = sel[sel[:, 1] == 0]
+        out.append(len(sel))
+    return out
+
+
+@pytest.mark.parametrize("policy", ["engine", "per1k"])
+@pytest.mark.parametrize("cus", [256, 108, 8])
+def test_page_policies_match_oracle(policy, cus):
+    rng = np.random.default_rng(11 + cus)
+    for trial in range(6):
+        n = int(rng.integers(1, 40))
+        ctx = np.exp(rng.uniform(np.log(20), np.log(40000), n)).astype(np.int64).tolist()
+        spec = wl.custom_spec("p", [1] * n, ctx, 4, 4, 64, 64, seed=trial)
+        lens = [c + 1 for c in ctx]
+        if policy == "engine":
+            want = host_heuristic(lens, num_sms=cus, min_chunk_size=256)
+            plan = plan_of(spec, target_cus=cus, split_policy=fgb.FG_SPLIT_ENGINE, max_splits=256)
+        else:
+            want = figure_rule(lens)
+            plan = plan_of(spec, target_cus=cus, split_policy=fgb.FG_SPLIT_PER_1K, max_splits=256)
+        got = _splits_per_seq(plan, n)
+        assert got == [_aligned(min(k, 256), L) for k, L in zip(want, lens)], (lens, want, got)
+        check_plan(plan, spec)
+
+
+def test_engine_policy_golden_case():
+    # the page's Step 4 harness input at 108 SMs and a 512-token minimum chunk
+    lens = [256, 1024, 4096, 8192]
+    spec = wl.custom_spec("g", [1] * 4, [x - 1 for x in lens], 4, 4, 64, 64, seed=1)
+    plan = plan_of(spec, target_cus=108, split_policy=fgb.FG_SPLIT_ENGINE,
+                   min_split_tokens=512, max_splits=256)
+    assert _splits_per_seq(plan, 4) == [_aligned(k, L) for k, L in zip([4, 8, 32, 64], lens)]
