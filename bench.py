@@ -235,6 +235,8 @@ def run_trace(args, torch, fgb, wl):
     lse = torch.empty((2048, hq), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
+    separate = args.separate_append
+
     def replay(record):
         keep, evs, host = [], [], []
         for p, (q, k, v) in zip(passes, inputs):
@@ -245,8 +247,11 @@ def run_trace(args, torch, fgb, wl):
             if record:
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
-            plan.upload(meta, stream)
-            fgb.kv_append(plan, meta, k, v, kp, vp, stream)
+            if separate:
+                plan.upload(meta, stream)
+                fgb.kv_append(plan, meta, k, v, kp, vp, stream)
+            else:
+                fgb.upload_append(plan, meta, k, v, kp, vp, stream)
             fgb.attention_ragged(plan, meta, q, kp, vp, out[:t], lse[:t], workspace=ws, stream=stream)
             if record:
                 e1.record(stream)
@@ -305,9 +310,10 @@ def knobs_of(args, fgb):
     return {"target_cus": args.target_cus, "split_policy": policy, "force_splits": args.force_splits}
 
 
-def measure_pass(torch, fgb, spec, tens, dev, stream, knobs, steps, warmup):
+def measure_pass(torch, fgb, spec, tens, dev, stream, knobs, steps, warmup, separate=False):
     """Set up pools and inputs of one pass, then time `steps` passes (plan,
-    upload, append, attention) back to back after `warmup` untimed ones.
+    upload + append in one launch, attention; `separate` uses the two-launch
+    upload and append) back to back after `warmup` untimed ones.
     Per-kernel times come from the library's HIP events on the launch stream."""
     def to_dev(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -339,8 +345,11 @@ def measure_pass(torch, fgb, spec, tens, dev, stream, knobs, steps, warmup):
         h0 = time.perf_counter()
         plan = fgb.Plan.from_spec(spec, **knobs)
         host_plan_s.append(time.perf_counter() - h0)
-        plan.upload(meta, stream)
-        fgb.kv_append(plan, meta, kn, vn, kp, vp, stream)
+        if separate:
+            plan.upload(meta, stream)
+            fgb.kv_append(plan, meta, kn, vn, kp, vp, stream)
+        else:
+            fgb.upload_append(plan, meta, kn, vn, kp, vp, stream)
         fgb.attention_ragged(plan, meta, q, kp, vp, out, lse, workspace=ws, stream=stream)
         keep.append(plan)
 
@@ -385,7 +394,8 @@ def run_sweep(args, torch, fgb, wl, dev, stream, knobs):
         spec = wl.config_spec(f"7b_budget{budget}")
         tens = wl.make_tensors(spec)
         alg = algorithmic(spec)
-        m = measure_pass(torch, fgb, spec, tens, dev, stream, knobs, args.steps, args.warmup)
+        m = measure_pass(torch, fgb, spec, tens, dev, stream, knobs, args.steps, args.warmup,
+                         args.separate_append)
         ku = kernel_us(m["kern"])
         pass_us = m["ms_per_step"] * 1e3
         rows.append({"budget": budget, "pass_us": round(pass_us, 2),
@@ -438,6 +448,8 @@ def main():
                     help="planner split-count policy (speed only; results are identical)")
     ap.add_argument("--force-splits", type=int, default=0,
                     help="static split count for every row group (FlashDecoding-style)")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="upload the plan and append K/V in two launches instead of one")
     ap.add_argument("--no-achievable", action="store_true",
                     help="skip the achievable-peak probes (copy and bf16 GEMM)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -480,7 +492,8 @@ def main():
     alg = algorithmic(spec)
     t, hq, d = spec.num_tokens, spec.num_q_heads, spec.head_dim
     knobs = knobs_of(args, fgb)
-    m = measure_pass(torch, fgb, spec, tens, dev, stream, knobs, args.steps, args.warmup)
+    m = measure_pass(torch, fgb, spec, tens, dev, stream, knobs, args.steps, args.warmup,
+                     args.separate_append)
     step, keep, kern, info = m["step"], m["keep"], m["kern"], m["info"]
     host_plan_s, ms_per_step = m["host_plan_s"], m["ms_per_step"]
 

@@ -21,6 +21,8 @@
  * the library:
  *     fg_plan_pass -> fg_plan_upload -> fg_kv_append -> fg_attention_ragged
  *     ... stream sync ... -> fg_plan_destroy
+ * or, with the first two device steps in one launch,
+ *     fg_plan_pass -> fg_upload_append -> fg_attention_ragged -> ...
  *
  * Conventions
  * -----------
@@ -169,6 +171,16 @@ fg_status fg_plan_upload(const fg_plan* plan, void* d_meta, void* stream);
 fg_status fg_kv_append(const fg_plan* plan, const void* d_meta,
                        const void* k_new, const void* v_new,
                        void* k_pool, void* v_pool, void* stream);
+
+/* fg_plan_upload followed by fg_kv_append, as one kernel launch (saves a launch
+ * and the gap between two kernels).  Arguments as for those two calls; on
+ * return d_meta holds the plan (once the stream gets there) and the pools hold
+ * the pass's new K/V, bit-exact as fg_kv_append writes them.  The append reads
+ * its run records from the pinned staging slot, so it does not wait for the
+ * metadata copy.  Plans over 1 MiB, or a process where pinned staging could
+ * not be allocated, fall back to the two separate steps. */
+fg_status fg_upload_append(const fg_plan* plan, void* d_meta, const void* k_new,
+                           const void* v_new, void* k_pool, void* v_pool, void* stream);
 
 /* Attention of every query row of the pass over its sequence's cached keys
  * 0 .. ctx + j (inclusive causal bound), read through the block tables

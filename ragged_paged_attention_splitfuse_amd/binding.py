@@ -75,6 +75,7 @@ SIGNATURES = {
     "fg_plan_info": (ctypes.c_int32, [ctypes.c_void_p, ctypes.POINTER(fg_plan_info_t)]),
     "fg_plan_upload": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "fg_kv_append": (ctypes.c_int32, [ctypes.c_void_p] * 7),
+    "fg_upload_append": (ctypes.c_int32, [ctypes.c_void_p] * 7),
     "fg_attention_ragged": (ctypes.c_int32, [ctypes.c_void_p] * 6 + [ctypes.c_int32, ctypes.c_void_p,
                                                                      ctypes.c_void_p, ctypes.c_size_t,
                                                                      ctypes.c_void_p]),
@@ -269,6 +270,26 @@ def fg_kv_append(plan, d_meta, k_new, v_new, k_pool, v_pool, stream=None):
                               _stream(stream)), "fg_kv_append")
 
 
+def fg_upload_append(plan, d_meta, k_new, v_new, k_pool, v_pool, stream=None, device="cuda"):
+    """fg_upload_append: plan upload and KV append in one launch.  d_meta is
+    allocated here (torch uint8) when None; returns it."""
+    t, hkv, d = plan.num_tokens, plan.num_kv_heads, plan.head_dim
+    kshape, vshape = pool_shapes(plan.num_blocks, hkv, plan.block_size, d)
+    if d_meta is None:
+        import torch
+        d_meta = torch.empty(max(16, plan.info["metadata_bytes"]), dtype=torch.uint8, device=device)
+    elif hasattr(d_meta, "numel") and d_meta.numel() * d_meta.element_size() < plan.info["metadata_bytes"]:
+        raise ValueError("metadata buffer too small")
+    _check_tensor(k_new, (t, hkv, d), "bf16", "k_new")
+    _check_tensor(v_new, (t, hkv, d), "bf16", "v_new")
+    _check_tensor(k_pool, kshape, "bf16", "k_pool")
+    _check_tensor(v_pool, vshape, "bf16", "v_pool")
+    _check(lib().fg_upload_append(plan.handle, _ptr(d_meta), _ptr(k_new), _ptr(v_new), _ptr(k_pool),
+                                  _ptr(v_pool), _stream(stream)), "fg_upload_append")
+    plan.meta = d_meta
+    return d_meta
+
+
 def fg_attention_ragged(plan, d_meta, q, k_pool, v_pool, out, lse=None, workspace=None,
                         stream=None, out_dtype=None):
     t, hq, hkv, d = plan.num_tokens, plan.num_q_heads, plan.num_kv_heads, plan.head_dim
@@ -310,4 +331,5 @@ def fg_profile_read():
 
 # short aliases used by tests and bench
 kv_append = fg_kv_append
+upload_append = fg_upload_append
 attention_ragged = fg_attention_ragged

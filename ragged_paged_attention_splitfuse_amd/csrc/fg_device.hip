@@ -675,12 +675,10 @@ __device__ __forceinline__ uint32_t pick_hi(uint32_t a, uint32_t b) {
 }
 
 template <int D, int B>
-__global__ __launch_bounds__(kThreads) void append_kernel(const RunRec* runs, const uint16_t* k_new,
-                                                           const uint16_t* v_new, uint16_t* kpool,
-                                                           uint16_t* vpool, int hkv) {
+__device__ __forceinline__ void append_run(const RunRec run, const int g, const uint16_t* k_new,
+                                           const uint16_t* v_new, uint16_t* kpool, uint16_t* vpool,
+                                           int hkv) {
   constexpr int CPR = D / 8;
-  const RunRec run = runs[blockIdx.x];
-  const int g = blockIdx.y;
   uint16_t* kdst = kpool + ((size_t(run.block) * hkv + g) * B + run.slot0) * D;
   for (int c = threadIdx.x; c < run.count * CPR; c += kThreads) {
     const int i = c / CPR, dc = c % CPR;
@@ -726,6 +724,34 @@ __global__ __launch_bounds__(kThreads) void append_kernel(const RunRec* runs, co
       }
     }
   }
+}
+
+// One work-group per (append run, kv head).
+template <int D, int B>
+__global__ __launch_bounds__(kThreads) void append_kernel(const RunRec* runs, const uint16_t* k_new,
+                                                           const uint16_t* v_new, uint16_t* kpool,
+                                                           uint16_t* vpool, int hkv) {
+  append_run<D, B>(runs[blockIdx.x], blockIdx.y, k_new, v_new, kpool, vpool, hkv);
+}
+
+// Plan upload and append in one launch.  Work-groups below n_copy copy the
+// metadata blob from the pinned host slot into the device buffer (for the
+// attention launch that follows); the others append run (i / hkv) of kv head
+// (i % hkv), reading their run record straight from the pinned slot, so they
+// do not depend on the copy.
+template <int D, int B>
+__global__ __launch_bounds__(kThreads) void upload_append_kernel(
+    const u32x4* __restrict__ blob_host, u32x4* __restrict__ blob_dev, unsigned chunks,
+    unsigned n_copy, const RunRec* runs_host, const uint16_t* k_new, const uint16_t* v_new,
+    uint16_t* kpool, uint16_t* vpool, int hkv) {
+  if (blockIdx.x < n_copy) {
+    const unsigned i = blockIdx.x * kThreads + threadIdx.x;
+    if (i < chunks) blob_dev[i] = blob_host[i];
+    return;
+  }
+  const unsigned w = blockIdx.x - n_copy;
+  append_run<D, B>(runs_host[w / unsigned(hkv)], int(w % unsigned(hkv)), k_new, v_new, kpool, vpool,
+                   hkv);
 }
 
 // ---------------------------------------------------------------- profiling
@@ -882,6 +908,52 @@ extern "C" fg_status fg_kv_append(const fg_plan* plan, const void* d_meta, const
   FG_SWITCH_DB(plan->head_dim, plan->block_size, FG_LAUNCH_APPEND);
 #undef FG_LAUNCH_APPEND
   return hipGetLastError() == hipSuccess ? FG_OK : FG_E_HIP;
+}
+
+extern "C" fg_status fg_upload_append(const fg_plan* plan, void* d_meta, const void* k_new,
+                                     const void* v_new, void* k_pool, void* v_pool, void* stream) {
+  if (!plan || !d_meta || !aligned16(d_meta)) return FG_E_INVALID;
+  if (plan->n_runs > 0 && (!k_new || !v_new || !k_pool || !v_pool || !aligned16(k_new) ||
+                           !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool)))
+    return FG_E_INVALID;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t bytes = plan->blob.size();
+  {
+    std::lock_guard<std::mutex> lk(g_stage_mu);
+    if (plan->n_runs > 0 && bytes <= kStageSlotBytes && stage_ready()) {
+      StageSlot& slot = g_stage[g_stage_next];
+      g_stage_next = (g_stage_next + 1) % kStageSlots;
+      if (slot.pending) {
+        if (hipEventSynchronize(slot.done) != hipSuccess) return FG_E_HIP;
+        slot.pending = false;
+      }
+      memcpy(slot.host, plan->blob.data(), bytes);
+      const unsigned chunks = unsigned((bytes + 15) / 16);
+      const unsigned n_copy = (chunks + kThreads - 1) / kThreads;
+      const RunRec* runs_host =
+          reinterpret_cast<const RunRec*>(static_cast<const uint8_t*>(slot.host) + plan->off_runs);
+      {
+        ProfScope prof(FG_KERNEL_APPEND, s);
+        const dim3 grid(n_copy + unsigned(plan->n_runs) * unsigned(plan->hkv));
+#define FG_LAUNCH_UPAPP(D_, B_)                                                                  \
+  hipLaunchKernelGGL((upload_append_kernel<D_, B_>), grid, dim3(kThreads), 0, s,                 \
+                     reinterpret_cast<const u32x4*>(slot.host), static_cast<u32x4*>(d_meta),      \
+                     chunks, n_copy, runs_host, static_cast<const uint16_t*>(k_new),              \
+                     static_cast<const uint16_t*>(v_new), static_cast<uint16_t*>(k_pool),          \
+                     static_cast<uint16_t*>(v_pool), plan->hkv)
+        FG_SWITCH_DB(plan->head_dim, plan->block_size, FG_LAUNCH_UPAPP);
+#undef FG_LAUNCH_UPAPP
+      }
+      if (hipGetLastError() != hipSuccess) return FG_E_HIP;
+      if (hipEventRecord(slot.done, s) != hipSuccess) return FG_E_HIP;
+      slot.pending = true;
+      return FG_OK;
+    }
+  }
+  // no staging (or an empty pass): the two separate steps
+  fg_status st = fg_plan_upload(plan, d_meta, stream);
+  if (st != FG_OK) return st;
+  return fg_kv_append(plan, d_meta, k_new, v_new, k_pool, v_pool, stream);
 }
 
 extern "C" fg_status fg_attention_ragged(const fg_plan* plan, const void* d_meta, const void* q,

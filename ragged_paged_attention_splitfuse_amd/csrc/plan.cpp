@@ -83,44 +83,48 @@ struct Pending {
 // CUs holding fewer items last.  Items after those rounds keep their order
 // and fill whichever CU frees a slot first.  Only speed depends on this.
 void place_resident_rounds(std::vector<Pending>& list, int cus) {
+  static_assert(kMfmaSlotsPerCu == 2, "CU bins hold two items");
   const size_t c = size_t(cus);
   const size_t m = std::min(list.size(), c * kMfmaSlotsPerCu);
   if (m <= c) return;
-  std::vector<size_t> idx(m);
-  std::iota(idx.begin(), idx.end(), size_t(0));
+  std::vector<uint32_t> idx(m);
+  std::iota(idx.begin(), idx.end(), 0u);
   std::stable_sort(idx.begin(), idx.end(),
-                   [&](size_t x, size_t y) { return list[x].cost > list[y].cost; });
-  std::vector<double> load(c, 0.0);
-  std::vector<std::vector<size_t>> bins(c);
-  // (load, cu) min-heap over CUs with a free slot; ties go to the lower cu.
-  using Entry = std::pair<double, size_t>;
-  std::vector<Entry> heap;
-  for (size_t u = 0; u < c; ++u) heap.push_back({0.0, u});
+                   [&](uint32_t x, uint32_t y) { return list[x].cost > list[y].cost; });
+  // The costliest c items open one bin each; the rest go, costliest first,
+  // to the least-loaded bin still holding one item (ties: lower bin).
+  std::vector<double> load(c);
+  std::vector<uint32_t> first(c), second(c, UINT32_MAX);
+  using Entry = std::pair<double, uint32_t>;
+  std::vector<Entry> heap(c);
+  for (size_t u = 0; u < c; ++u) {
+    first[u] = idx[u];
+    load[u] = list[idx[u]].cost;
+    heap[u] = {load[u], uint32_t(u)};
+  }
   auto cmp = [](const Entry& x, const Entry& y) {
     return x.first != y.first ? x.first > y.first : x.second > y.second;
   };
   std::make_heap(heap.begin(), heap.end(), cmp);
-  for (size_t i : idx) {
+  for (size_t i = c; i < m; ++i) {
     std::pop_heap(heap.begin(), heap.end(), cmp);
-    Entry e = heap.back();
+    const uint32_t u = heap.back().second;
     heap.pop_back();
-    bins[e.second].push_back(i);
-    e.first += list[i].cost;
-    if (bins[e.second].size() < size_t(kMfmaSlotsPerCu)) {
-      heap.push_back(e);
-      std::push_heap(heap.begin(), heap.end(), cmp);
-    }
+    second[u] = idx[i];
   }
-  // Fuller bins first: round r covers positions r*C .. r*C + (items in round) - 1.
-  std::stable_sort(bins.begin(), bins.end(),
-                   [](const std::vector<size_t>& x, const std::vector<size_t>& y) {
-                     return x.size() > y.size();
-                   });
+  // Bins holding two items first: round 0 takes every bin's first item, round
+  // 1 the second items, so bin u's pair sits at positions u and u + c.
+  std::vector<uint32_t> order(c);
+  size_t lo = 0, hi = c;
+  for (size_t u = 0; u < c; ++u) {
+    if (second[u] != UINT32_MAX) order[lo++] = uint32_t(u);
+    else order[--hi] = uint32_t(u);
+  }
+  std::reverse(order.begin() + lo, order.end());   // keep single bins in bin order
   std::vector<Pending> placed;
   placed.reserve(m);
-  for (size_t r = 0; r < size_t(kMfmaSlotsPerCu); ++r)
-    for (size_t u = 0; u < c; ++u)
-      if (r < bins[u].size()) placed.push_back(list[bins[u][r]]);
+  for (size_t k = 0; k < c; ++k) placed.push_back(list[first[order[k]]]);
+  for (size_t k = 0; k < lo; ++k) placed.push_back(list[second[order[k]]]);
   std::copy(placed.begin(), placed.end(), list.begin());
 }
 
@@ -200,6 +204,7 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
 
     // ---- append runs: consecutive new tokens of a sequence within one block
     std::vector<RunRec> runs;
+    runs.reserve(size_t(used_blocks));
     for (int s = 0; s < S; ++s) {
       const SeqRec& r = seqs[s];
       int64_t p = r.ctx;
@@ -220,6 +225,7 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
     // decode group streams them from HBM, a full 128-row tile spends about the
     // same time on matrix-core work per token at the MI355X flop:byte ratio)
     std::vector<Group> groups;
+    groups.reserve(size_t(S) * size_t(d->num_kv_heads) * 2);
     double total_cost = 0.0;
     for (int s = 0; s < S; ++s) {
       const SeqRec& r = seqs[s];
@@ -281,6 +287,8 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
             ? 1e300
             : std::max(1.0, tile_cost / (double(target_cus) * kMfmaSlotsPerCu));
     std::vector<Pending> mfma, valu;
+    mfma.reserve(groups.size());
+    valu.reserve(groups.size() * 2);
     std::vector<MergeRec> merges;
     int64_t partial_rows = 0;
     int32_t merge_groups = 0;

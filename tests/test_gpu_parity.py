@@ -82,6 +82,40 @@ def test_append_is_bit_exact(name):
     assert np.array_equal(G.to_host_bits(vp), vref)
 
 
+@pytest.mark.parametrize("name", ["tiny", "mha_d128_b64_mixed", "gqa8_d128_b64_mixed", "gqa4_d64_b16_mixed"])
+def test_upload_append_matches_separate_steps(name):
+    # one launch (fg_upload_append) against fg_plan_upload + fg_kv_append:
+    # same metadata bytes, bit-identical pools, bit-identical attention
+    spec = SMALL_SPECS[name]()
+    _log(f"[case] fused upload+append {name}")
+    tens = wl.make_tensors(spec)
+    q, kn, vn = G.to_dev(tens.q), G.to_dev(tens.k_new), G.to_dev(tens.v_new)
+    pools = []
+    for fused in (False, True):
+        kp, vp = G.gpu_pools(spec, poison=True)
+        G.fill_history(spec, tens, kp, vp)
+        plan = fgb.Plan.from_spec(spec, target_cus=G.PLAN_CUS)
+        if fused:
+            meta = fgb.upload_append(plan, None, kn, vn, kp, vp)
+        else:
+            meta = plan.upload()
+            fgb.kv_append(plan, meta, kn, vn, kp, vp)
+        out = torch.full((spec.num_tokens, spec.num_q_heads, spec.head_dim), float("nan"), device="cuda")
+        lse = torch.full((spec.num_tokens, spec.num_q_heads), float("nan"), device="cuda")
+        fgb.attention_ragged(plan, meta, q, kp, vp, out, lse)
+        torch.cuda.synchronize()
+        nbytes = plan.info["metadata_bytes"]
+        pools.append((G.to_host_bits(kp), G.to_host_bits(vp), meta[:nbytes].cpu().numpy(),
+                      out.cpu(), lse.cpu()))
+        plan.close()
+    (k0, v0, m0, o0, l0), (k1, v1, m1, o1, l1) = pools
+    assert np.array_equal(m0, m1)
+    assert np.array_equal(k0, k1) and np.array_equal(v0, v1)
+    kref, vref = oracle_pools(spec, tens, poison=True)
+    assert np.array_equal(k1, kref) and np.array_equal(v1, vref)
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+
+
 @pytest.mark.parametrize("k", [1, 2, 3, 7, 64])
 def test_forced_split_counts(k):
     spec = SMALL_SPECS["mha_d128_b64_mixed"]()
