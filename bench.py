@@ -213,7 +213,10 @@ def run_trace(args, torch, fgb, wl):
     hq = hkv = 32
     d, bs, seed = 128, 64, 5
     reqs = sf.trace_requests()
-    passes, nb = sf.schedule(reqs, clients=32, budget=2048, block_size=bs, seed=seed)
+    arrivals = {}
+    passes, nb = sf.schedule(reqs, clients=32, budget=2048, block_size=bs, seed=seed,
+                             policy=args.serve_policy, arrivals=arrivals)
+    t_max = max(p.num_tokens for p in passes)
     kshape, vshape = fgb.pool_shapes(nb, hkv, bs, d)
     kp = torch.zeros(kshape, dtype=torch.bfloat16, device=dev)
     vp = torch.zeros(vshape, dtype=torch.bfloat16, device=dev)
@@ -231,8 +234,8 @@ def run_trace(args, torch, fgb, wl):
         pl.close()
     meta = torch.empty(max_meta, dtype=torch.uint8, device=dev)
     ws = torch.empty(max_ws, dtype=torch.uint8, device=dev)
-    out = torch.empty((2048, hq, d), dtype=torch.float32, device=dev)
-    lse = torch.empty((2048, hq), dtype=torch.float32, device=dev)
+    out = torch.empty((t_max, hq, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((t_max, hq), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
     separate = args.separate_append
@@ -272,6 +275,7 @@ def run_trace(args, torch, fgb, wl):
     fgb.fg_profile_enable(False)
     kern = fgb.fg_profile_read()
     per = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    serving = sf.serving_metrics(reqs, sf.composition_of(passes), arrivals, per)
     toks = sum(p.num_tokens for p in passes)
     kv_bytes = sum(int(np.sum(p.q_lens.astype(np.int64) + p.ctx_lens)) * hkv * d * 4 for p in passes)
     flops = sum(4 * d * hq * int(np.sum(p.q_lens.astype(np.int64) * p.ctx_lens
@@ -283,7 +287,8 @@ def run_trace(args, torch, fgb, wl):
         "n_gpus": 1, "steps": len(passes), "warmup": args.warmup,
         "ms_per_step": round(wall * 1e3 / len(passes), 5), "higher_is_better": False,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "trace512", "requests": len(reqs), "clients": 32, "budget": 2048,
+        "config": {"workload": "trace512", "policy": args.serve_policy, "requests": len(reqs),
+                   "clients": 32, "budget": 2048, "max_pass_tokens": t_max,
                    "q_heads": hq, "kv_heads": hkv, "head_dim": d, "block_size": bs,
                    "passes": len(passes), "pool_blocks": nb},
         "roofline": None, "cpu_baseline": None,
@@ -298,6 +303,7 @@ def run_trace(args, torch, fgb, wl):
             "attn_gbs_avg": round(kv_bytes / (attn_ms * 1e-3) / 1e9, 1) if attn_ms else None,
             "attn_tflops_avg": round(flops / (attn_ms * 1e-3) / 1e12, 2) if attn_ms else None,
             "kv_bytes_total": kv_bytes, "flops_total": flops,
+            "serving_on_device_timeline": serving,
         },
     }
     keep.clear()
@@ -450,6 +456,8 @@ def main():
                     help="static split count for every row group (FlashDecoding-style)")
     ap.add_argument("--separate-append", action="store_true",
                     help="upload the plan and append K/V in two launches instead of one")
+    ap.add_argument("--serve-policy", choices=["splitfuse", "orca", "prefill_first"],
+                    default="splitfuse", help="pass composition of the trace512 replay")
     ap.add_argument("--no-achievable", action="store_true",
                     help="skip the achievable-peak probes (copy and bf16 GEMM)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),

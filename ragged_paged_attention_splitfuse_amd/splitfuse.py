@@ -69,30 +69,78 @@ class _Live:
         self.admitted = admitted
 
 
-def compose(requests, clients=32, budget=2048):
-    """Pass composition only: list of [(rid, ctx, q_len, is_decode), ...]."""
+POLICIES = ("splitfuse", "orca", "prefill_first")
+
+
+def compose(requests, clients=32, budget=2048, policy="splitfuse", arrivals=None):
+    """Pass composition only: list of [(rid, ctx, q_len, is_decode), ...].
+
+    policy:
+      "splitfuse"      Dynamic SplitFuse: all decodes, then prompt chunks fill
+                       the budget exactly (long prompts split over passes).
+      "orca"           iteration-level batching without splitting: all decodes
+                       plus whole prompts in admission order while they fit
+                       the budget; a prompt that fits no pass runs whole anyway.
+      "prefill_first"  prefill-prioritising batching: while any live request
+                       has prompt left, a pass holds only whole prompts (at
+                       least one, as many as fit); decodes wait.
+    The two baselines are the compositions the pages contrast with SplitFuse
+    (research summary, "Summary": prompts that pause generation, and whole
+    prompts run beside generation making some passes very large).
+    If `arrivals` is a dict, it receives rid -> index of the first pass the
+    request could have joined (its client submitted it just before that pass).
+    """
+    if policy not in POLICIES:
+        raise ValueError(f"unknown policy {policy!r}")
     pending = list(requests)
     live = []
     order = 0
     passes = []
     for _ in range(min(clients, len(pending))):
-        live.append(_Live(pending.pop(0), order))
+        req = pending.pop(0)
+        live.append(_Live(req, order))
+        if arrivals is not None:
+            arrivals[req.rid] = 0
         order += 1
     while live:
+        decodes = [(lv, lv.req.prompt + lv.decodes_done, 1, True) for lv in live
+                   if lv.prompt_done == lv.req.prompt and lv.decodes_done < lv.req.output - 1]
+        waiting = [lv for lv in live if lv.prompt_done < lv.req.prompt]   # admission order
         seqs = []
-        for lv in live:
-            if lv.prompt_done == lv.req.prompt and lv.decodes_done < lv.req.output - 1:
-                seqs.append((lv, lv.req.prompt + lv.decodes_done, 1, True))
-        left = budget - len(seqs)
-        if left < 0:
-            raise ValueError("more decodes than the token budget")
-        for lv in live:                      # admission order == list order
-            if left == 0:
-                break
-            if lv.prompt_done < lv.req.prompt:
+        if policy == "splitfuse":
+            seqs = list(decodes)
+            left = budget - len(seqs)
+            if left < 0:
+                raise ValueError("more decodes than the token budget")
+            for lv in waiting:
+                if left == 0:
+                    break
                 n = min(lv.req.prompt - lv.prompt_done, left)
                 seqs.append((lv, lv.prompt_done, n, False))
                 left -= n
+        elif policy == "orca":
+            seqs = list(decodes)
+            used, any_prompt = len(seqs), False
+            for lv in waiting:
+                n = lv.req.prompt
+                if used + n <= budget or not any_prompt:
+                    seqs.append((lv, 0, n, False))
+                    used += n
+                    any_prompt = True
+                if used >= budget:
+                    break
+        else:
+            if waiting:
+                used = 0
+                for lv in waiting:
+                    n = lv.req.prompt
+                    if used == 0 or used + n <= budget:
+                        seqs.append((lv, 0, n, False))
+                        used += n
+                    if used >= budget:
+                        break
+            else:
+                seqs = list(decodes)
         if not seqs:
             raise RuntimeError("scheduler made no progress")
         passes.append([(lv.req.rid, ctx, n, dec) for lv, ctx, n, dec in seqs])
@@ -107,18 +155,75 @@ def compose(requests, clients=32, budget=2048):
         for lv in finished:
             live.remove(lv)
             if pending:
-                live.append(_Live(pending.pop(0), order))
+                req = pending.pop(0)
+                live.append(_Live(req, order))
+                if arrivals is not None:
+                    arrivals[req.rid] = len(passes)
                 order += 1
     return passes
 
 
-def schedule(requests, clients=32, budget=2048, block_size=64, seed=5, slack=1.25):
+def serving_metrics(requests, comp, arrivals, pass_us):
+    """User-facing metrics of a composed trace on a measured timeline.
+
+    comp: compose() output; arrivals: its rid -> first-joinable pass index;
+    pass_us: duration of each pass in microseconds (passes back to back).
+    A request's first output token comes at the end of the pass holding its
+    last prompt token, each later token at the end of its decode pass.
+    TTFT = first-token time - arrival time; TPOT = mean gap between its output
+    tokens (requests with more than one); token gaps pool every such gap for
+    the tail; latency = last-token time - arrival time.  Time to first token
+    and a steady token pace are the user-facing measures the research summary
+    names (idea I4); the pages' absolute SLA figures belong to whole-model
+    passes and are not used here.
+    """
+    ends = np.cumsum(np.asarray(pass_us, dtype=np.float64))
+    prompt_len = {r.rid: r.prompt for r in requests}
+
+    def start(i):
+        return ends[i - 1] if i > 0 else 0.0
+
+    first, last, gaps, ntok = {}, {}, [], {}
+    for i, p in enumerate(comp):
+        for rid, ctx, n, dec in p:
+            if dec:
+                gaps.append(ends[i] - last[rid])
+                last[rid] = ends[i]
+                ntok[rid] += 1
+            elif rid in prompt_len and ctx + n == prompt_len[rid]:
+                first[rid] = last[rid] = ends[i]
+                ntok[rid] = 1
+    ttft, tpot, lat = [], [], []
+    for r in requests:
+        a = start(arrivals[r.rid])
+        ttft.append(first[r.rid] - a)
+        lat.append(last[r.rid] - a)
+        if ntok[r.rid] > 1:
+            tpot.append((last[r.rid] - first[r.rid]) / (ntok[r.rid] - 1))
+
+    def pct(x):
+        x = np.asarray(x, dtype=np.float64)
+        return {"mean": round(float(x.mean()), 2), "p50": round(float(np.percentile(x, 50)), 2),
+                "p90": round(float(np.percentile(x, 90)), 2), "p95": round(float(np.percentile(x, 95)), 2),
+                "p99": round(float(np.percentile(x, 99)), 2), "max": round(float(x.max()), 2)}
+
+    total = float(ends[-1]) if len(ends) else 0.0
+    out_tokens = sum(r.output for r in requests)
+    return {"ttft_us": pct(ttft), "tpot_us": pct(tpot), "token_gap_us": pct(gaps),
+            "latency_us": pct(lat), "total_us": round(total, 1),
+            "requests_per_s": round(len(requests) / (total * 1e-6), 2) if total else None,
+            "output_tokens_per_s": round(out_tokens / (total * 1e-6), 1) if total else None,
+            "passes": len(comp)}
+
+
+def schedule(requests, clients=32, budget=2048, block_size=64, seed=5, slack=1.25,
+             policy="splitfuse", arrivals=None):
     """Compose passes and give every sequence its block table.
 
     Returns (passes, num_blocks).  The pool holds slack x the peak number of
     blocks live at once; blocks come from a shuffled free list.
     """
-    comp = compose(requests, clients, budget)
+    comp = compose(requests, clients, budget, policy, arrivals)
     last = {}
     for i, p in enumerate(comp):
         for rid, _, _, _ in p:
@@ -159,3 +264,9 @@ def schedule(requests, clients=32, budget=2048, block_size=64, seed=5, slack=1.2
         for rid in finals[i]:
             free.extend(tables.pop(rid))
     return out, num_blocks
+
+
+def composition_of(passes):
+    """schedule() output back in compose() form: [(rid, ctx, q_len, is_decode), ...]."""
+    return [[(int(p.rids[s]), int(p.ctx_lens[s]), int(p.q_lens[s]), s < p.num_decodes)
+             for s in range(len(p.rids))] for p in passes]

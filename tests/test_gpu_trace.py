@@ -77,3 +77,20 @@ def test_full_trace_sampled_passes():
         chunks = list(range(p.num_decodes, len(p.q_lens)))
         seqs = sorted(set(chunks[:3] + list(range(min(3, p.num_decodes)))))
         _check_pass(p, got[i], seqs, [0, 21], 5, 128, 64)
+
+
+@pytest.mark.parametrize("policy", ["orca", "prefill_first"])
+def test_baseline_composition_oversized_passes(policy):
+    # the baselines run whole prompts, so some passes exceed the 2048 budget;
+    # those passes go through the same library calls and stay on the oracle
+    reqs = sf.trace_requests(40, seed=7)
+    passes, nb = sf.schedule(reqs, clients=16, budget=2048, block_size=64, seed=7, policy=policy)
+    big = max(range(len(passes)), key=lambda i: (passes[i].num_tokens, -i))
+    keep = sorted({big, min(len(passes) - 1, big + 3)})
+    _log(f"[case] {policy} passes={len(passes)} big={big} tokens={passes[big].num_tokens} keep={keep}")
+    assert passes[big].num_tokens > 2048
+    got = _replay(passes, nb, 32, 32, 128, 64, 7, keep)
+    for i in keep:
+        p = passes[i]
+        seqs = list(range(min(4, len(p.q_lens))))
+        _check_pass(p, got[i], seqs, [3], 7, 128, 64)

@@ -103,3 +103,65 @@ def test_hash_generator_numpy_matches_torch():
                   for r, q in zip(rids, pos)])
     t = wl.hash_normal_bf16_torch(7, wl.KIND_K, rids, pos, 4, 64, "cpu")
     assert np.array_equal(a, t.view(torch.int16).numpy().view(np.uint16))
+
+
+# ---- baseline compositions and user-facing metrics
+
+def _walk(requests, comp):
+    """Replay a composition; check prompts whole-or-chunked in order and
+    O - 1 decodes after the prompt; return per-pass (tokens, prompt kinds)."""
+    req = {r.rid: r for r in requests}
+    done, dec = defaultdict(int), defaultdict(int)
+    for p in comp:
+        for rid, ctx, n, is_dec in p:
+            r = req[rid]
+            if is_dec:
+                assert done[rid] == r.prompt and ctx == r.prompt + dec[rid]
+                dec[rid] += 1
+            else:
+                assert ctx == done[rid] and n >= 1
+                done[rid] += n
+        assert len({rid for rid, _, _, _ in p}) == len(p)
+    assert all(done[r] == req[r].prompt and dec[r] == req[r].output - 1 for r in req)
+
+
+@pytest.mark.parametrize("policy", ["orca", "prefill_first"])
+def test_baseline_policies_run_whole_prompts(policy):
+    reqs = sf.trace_requests(80, seed=9, prompt_mean=900, prompt_sd=400, out_mean=10, out_sd=3)
+    comp = sf.compose(reqs, clients=8, budget=1024, policy=policy)
+    _walk(reqs, comp)
+    for p in comp:
+        prompts = [(ctx, n) for _, ctx, n, d in p if not d]
+        decodes = [1 for *_, d in p if d]
+        assert all(ctx == 0 for ctx, _ in prompts)            # never split
+        tokens = sum(n for _, n in prompts) + len(decodes)
+        if len(prompts) > 1:
+            assert tokens <= 1024                              # packing stays in budget
+        if policy == "prefill_first":
+            assert not (prompts and decodes)                   # prompts pause generation
+
+
+def test_splitfuse_never_exceeds_budget_but_baselines_may():
+    reqs = sf.trace_requests(64, seed=3)
+    sizes = {pol: max(sum(n for _, _, n, _ in p) for p in sf.compose(reqs, 32, 2048, pol))
+             for pol in sf.POLICIES}
+    assert sizes["splitfuse"] == 2048
+    assert sizes["orca"] > 2048 and sizes["prefill_first"] > 2048
+
+
+def test_serving_metrics_on_a_hand_timeline():
+    # request 0: prompt 3, 3 outputs; request 1 arrives after 0 finishes (1 client)
+    reqs = [sf.TraceRequest(0, 3, 3), sf.TraceRequest(1, 2, 1)]
+    arr = {}
+    comp = sf.compose(reqs, clients=1, budget=2, policy="splitfuse", arrivals=arr)
+    # passes: [0: prompt 0..1], [0: prompt 2], [0 decode], [0 decode], [1: prompt 0..1]
+    assert [[(r, c, n, d) for r, c, n, d in p] for p in comp] == [
+        [(0, 0, 2, False)], [(0, 2, 1, False)], [(0, 3, 1, True)], [(0, 4, 1, True)], [(1, 0, 2, False)]]
+    assert arr == {0: 0, 1: 4}
+    m = sf.serving_metrics(reqs, comp, arr, [10, 20, 30, 40, 50])
+    # ends: 10, 30, 60, 100, 150.  r0: first token 30, then 60, 100 -> TTFT 30, TPOT 35
+    # r1: arrives at 100 (start of pass 4), first (and only) token at 150 -> TTFT 50
+    assert m["ttft_us"]["max"] == 50 and m["ttft_us"]["mean"] == 40
+    assert m["tpot_us"]["mean"] == 35
+    assert sorted([m["token_gap_us"]["max"], m["token_gap_us"]["p50"]]) == [35, 40]
+    assert m["latency_us"]["max"] == 100 and m["total_us"] == 150
