@@ -250,3 +250,49 @@ def test_full_size_decode64_sampled_sequences():
     sub, st, rows = G.subset(spec, tens, picks)
     o_ref, l_ref = G.oracle_pass(sub, st)
     compare(out, lse, o_ref, l_ref, f"7b_decode64 seqs {picks}", rows=rows)
+
+
+# ---------------------------------------------------------------- edge shapes
+
+def test_long_context_decode_uses_many_splits():
+    # a 120k-token decode next to short ones: the planner splits it up to the
+    # split cap, and the merge combines all parts
+    spec = wl.custom_spec("long", [1, 1, 3], [120000, 40, 70], 4, 4, 128, 64, seed=31)
+    _log(f"[case] long decode kv={int(spec.kv_lens.max())}")
+    tens, _, _, out, lse, plan = G.full_gpu_pass(spec, target_cus=256)
+    _log(f"[plan] {plan.info}")
+    assert plan.info["max_splits_used"] >= 16
+    o_ref, l_ref = G.oracle_pass(spec, tens)
+    compare(out, lse, o_ref, l_ref, "long decode")
+
+
+@pytest.mark.parametrize("hq,hkv", [(32, 1), (32, 2)])
+def test_mqa_and_wide_gqa_groups(hq, hkv):
+    # G = 32 and 16: a decode is a 32- or 16-row group (one-wave matrix-core
+    # item), a chunk row expands into G packed rows
+    spec = wl.custom_spec("wide", [1, 5, 1, 37], [900, 300, 0, 120], hq, hkv, 128, 64, seed=32)
+    _log(f"[case] hq={hq} hkv={hkv}")
+    tens, _, _, out, lse, plan = G.full_gpu_pass(spec, target_cus=64)
+    assert plan.info["num_mfma_items"] > 0
+    o_ref, l_ref = G.oracle_pass(spec, tens)
+    compare(out, lse, o_ref, l_ref, f"hq={hq} hkv={hkv}")
+
+
+def test_scale_override():
+    spec = wl.custom_spec("scale", [1, 70], [500, 90], 4, 2, 128, 32, seed=33, scale=0.3)
+    tens, _, _, out, lse, plan = G.full_gpu_pass(spec)
+    o_ref, l_ref = G.oracle_pass(spec, tens)
+    compare(out, lse, o_ref, l_ref, "scale 0.3")
+
+
+def test_budget8192_pass_sampled_heads():
+    # the largest token-budget sweep point: an 8176-token chunk at context 0
+    # plus 16 decodes; the oracle recomputes two q heads of every row
+    spec = wl.config_spec("7b_budget8192")
+    _log(f"[case] 7b_budget8192 T={spec.num_tokens}")
+    tens, _, _, out, lse, plan = G.full_gpu_pass(spec)
+    kp, vp = oracle_pools(spec, tens, poison=True)
+    heads = [0, 29]
+    o_ref, l_ref = ora.attend(tens.q, kp, vp, spec.q_lens, spec.ctx_lens, spec.block_tables,
+                              spec.block_size, spec.num_kv_heads, heads=heads)
+    compare(out[:, heads], lse[:, heads], o_ref[:, heads], l_ref[:, heads], "budget 8192 heads 0,29")
