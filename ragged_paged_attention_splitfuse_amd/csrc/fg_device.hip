@@ -340,7 +340,7 @@ __device__ void valu_item(const AttnArgs& a, const ItemRec& it, float* smem) {
 // ----------------------------------------------------------------------------
 // Matrix-core path: up to 128 packed query rows (32 per wavefront, one per lane
 // pair l, l^32) of one (sequence, kv head) over the item's KV range, in
-// 64-token stages double-buffered through LDS.
+// 64-token stages double-buffered in LDS.
 //
 // Stage layout in LDS (bf16): K rows [64][D+8] with the 32 tokens of each half
 // stored at row perm32(t) (bits 2 and 3 swapped), then V^T rows [D][64+8].
@@ -362,6 +362,12 @@ struct MfmaLds {
   static constexpr int STAGE = KT + VT;
   static constexpr int BYTES = 2 * STAGE * 2;
 };
+
+__device__ __forceinline__ void lds_dma16(const uint16_t* src, uint16_t* lds_seg) {
+  using gptr = const void __attribute__((address_space(1)))*;
+  using lptr = void __attribute__((address_space(3)))*;
+  __builtin_amdgcn_global_load_lds((gptr)src, (lptr)lds_seg, 16, 0, 0);
+}
 
 template <int D, int B>
 __device__ void mfma_item(const AttnArgs& a, const ItemRec& it, uint16_t* lds) {
@@ -400,57 +406,31 @@ __device__ void mfma_item(const AttnArgs& a, const ItemRec& it, uint16_t* lds) {
   const size_t kv_head_base = size_t(g);
   u32x4 kst[KCH], vst[VCH];
 
-  // Global -> register staging of one 64-token stage.  Chunk c of this thread
-  // is 16-byte chunk ch = tid + 256 c of the stage.  With B == 64 a stage is
-  // exactly one block, and both its K rows and its V^T rows are one contiguous
-  // region of the block, so chunk ch sits at element offset 8 * ch of it.
-  // Only the final stage of a sequence (past kv_len) needs bounds checks.
+  // Global -> register staging of one 64-token stage, for B < 64 (a stage then
+  // spans 64 / B blocks; each chunk resolves its own block).  Chunk c of this
+  // thread is 16-byte chunk ch = tid + 256 c of the stage.  Only the final
+  // stage of a sequence (past kv_len) needs bounds checks.
   auto load_stage = [&](int tb) {
     const bool full = tb + kKvTile <= kv_valid;
-    if constexpr (B == kKvTile) {
-      const size_t tile = (size_t(bt[tb / B]) * a.hkv + kv_head_base) * (size_t(B) * D);
-      const uint16_t* kb = a.kpool + tile;
-      const uint16_t* vb = a.vpool + tile;
-      if (full) {
 #pragma unroll
-        for (int c = 0; c < KCH; ++c) kst[c] = ld16(kb + 8 * (tid + kThreads * c));
-#pragma unroll
-        for (int c = 0; c < VCH; ++c) vst[c] = ld16(vb + 8 * (tid + kThreads * c));
-        return;
+    for (int c = 0; c < KCH; ++c) {
+      const int ch = tid + kThreads * c;
+      const int tok = ch / CPR, dc = ch % CPR, p = tb + tok;
+      kst[c] = u32x4{0u, 0u, 0u, 0u};
+      if (full || p < kv_valid) {
+        const int blk = bt[p / B];
+        kst[c] = ld16(a.kpool + ((size_t(blk) * a.hkv + kv_head_base) * B + p % B) * D + 8 * dc);
       }
+    }
 #pragma unroll
-      for (int c = 0; c < KCH; ++c) {
-        const int ch = tid + kThreads * c;
-        kst[c] = (tb + ch / CPR < kv_valid) ? ld16(kb + 8 * ch) : u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int c = 0; c < VCH; ++c) {
-        const int ch = tid + kThreads * c;
-        const int p = tb + 8 * (ch % (kKvTile / 8));
-        vst[c] = (p < kv_valid) ? zero_tail(ld16(vb + 8 * ch), p, kv_valid) : u32x4{0u, 0u, 0u, 0u};
-      }
-    } else {
-      // B < 64: the stage spans 64 / B blocks; resolve each chunk's block.
-#pragma unroll
-      for (int c = 0; c < KCH; ++c) {
-        const int ch = tid + kThreads * c;
-        const int tok = ch / CPR, dc = ch % CPR, p = tb + tok;
-        kst[c] = u32x4{0u, 0u, 0u, 0u};
-        if (full || p < kv_valid) {
-          const int blk = bt[p / B];
-          kst[c] = ld16(a.kpool + ((size_t(blk) * a.hkv + kv_head_base) * B + p % B) * D + 8 * dc);
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < VCH; ++c) {
-        const int ch = tid + kThreads * c;
-        const int d = ch / (kKvTile / 8), tc = ch % (kKvTile / 8), p = tb + 8 * tc;
-        vst[c] = u32x4{0u, 0u, 0u, 0u};
-        if (full || p < kv_valid) {
-          const int blk = bt[p / B];
-          vst[c] = ld16(a.vpool + ((size_t(blk) * a.hkv + kv_head_base) * D + d) * B + p % B);
-          if (!full && p + 8 > kv_valid) vst[c] = zero_tail(vst[c], p, kv_valid);
-        }
+    for (int c = 0; c < VCH; ++c) {
+      const int ch = tid + kThreads * c;
+      const int d = ch / (kKvTile / 8), tc = ch % (kKvTile / 8), p = tb + 8 * tc;
+      vst[c] = u32x4{0u, 0u, 0u, 0u};
+      if (full || p < kv_valid) {
+        const int blk = bt[p / B];
+        vst[c] = ld16(a.vpool + ((size_t(blk) * a.hkv + kv_head_base) * D + d) * B + p % B);
+        if (!full && p + 8 > kv_valid) vst[c] = zero_tail(vst[c], p, kv_valid);
       }
     }
   };
@@ -479,12 +459,77 @@ __device__ void mfma_item(const AttnArgs& a, const ItemRec& it, uint16_t* lds) {
   constexpr uint32_t kOnePair = 0x3F803F80u;  // two bf16 1.0
   float lrnd = 0.f;  // row sum of the bf16-rounded probabilities
 
-  load_stage(it.kv0);
-  store_stage(0);
+  // With B == 64 a stage is one block, and the memory system writes it
+  // straight into the padded LDS layout (global_load_lds_dwordx4: lane l's 16
+  // bytes land at its wave's 1 KiB segment base + 16 l, from an address the
+  // lane picks), so no staging registers are held across the stage.  Segment
+  // sg of a stage is written by wave sg % 4; lane l fills stage unit
+  // u = 64 sg + l, i.e. row u / U, column unit u % U of the padded rows
+  // (U = D/8 + 1 units per K row, 9 per V^T row); a lane whose unit is row
+  // padding loads the row's last data unit again.  Each thread's offsets
+  // inside a block are fixed, so they are computed once.  V slots past kv_len
+  // are zeroed in LDS afterwards by the lane that loaded them (they may hold
+  // anything).  Other block sizes stage through registers (load_stage /
+  // store_stage above).
+  constexpr int KU = L::KS / 8, VU = L::VS / 8;
+  constexpr int K_SEGS = L::KT / 512, V_SEGS = L::VT / 512;
+  static_assert(K_SEGS * 512 == L::KT && V_SEGS * 512 == L::VT, "stage regions in whole KiB");
+  constexpr int KSEG_W = (K_SEGS + kWaves - 1) / kWaves, VSEG_W = (V_SEGS + kWaves - 1) / kWaves;
+  int koff[KSEG_W], voff[VSEG_W];
+  if constexpr (B == kKvTile) {
+#pragma unroll
+    for (int i = 0; i < KSEG_W; ++i) {
+      const int u = 64 * (i * kWaves + wave) + lane;
+      const int rr = u / KU, tok = (rr & 32) | perm32(rr & 31);
+      koff[i] = tok * D + 8 * min(u % KU, D / 8 - 1);
+    }
+#pragma unroll
+    for (int i = 0; i < VSEG_W; ++i) {
+      const int u = 64 * (i * kWaves + wave) + lane;
+      voff[i] = (u / VU) * B + 8 * min(u % VU, kKvTile / 8 - 1);
+    }
+  }
+  auto dma_stage = [&](int tb, int buf) {
+    const size_t tile = (size_t(bt[tb / B]) * a.hkv + kv_head_base) * (size_t(B) * D);
+    uint16_t* kt = lds + buf * L::STAGE;
+    uint16_t* vt = kt + L::KT;
+#pragma unroll
+    for (int i = 0; i < KSEG_W; ++i)
+      if (i * kWaves + wave < K_SEGS) lds_dma16(a.kpool + tile + koff[i], kt + (i * kWaves + wave) * 512);
+#pragma unroll
+    for (int i = 0; i < VSEG_W; ++i)
+      if (i * kWaves + wave < V_SEGS) lds_dma16(a.vpool + tile + voff[i], vt + (i * kWaves + wave) * 512);
+  };
+  auto fix_v_tail = [&](int tb, int buf) {
+    if (tb + kKvTile <= kv_valid) return;
+    uint16_t* vt = lds + buf * L::STAGE + L::KT;
+#pragma unroll
+    for (int i = 0; i < VSEG_W; ++i) {
+      const int u = 64 * (i * kWaves + wave) + lane;
+      const int col = u % VU;
+      if (i * kWaves + wave < V_SEGS && col < kKvTile / 8 && tb + 8 * col + 8 > kv_valid) {
+        uint16_t* dst = vt + 8 * u;
+        st16(dst, zero_tail(ld16(dst), tb + 8 * col, kv_valid));
+      }
+    }
+  };
+  if constexpr (B == kKvTile) {
+    dma_stage(it.kv0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    fix_v_tail(it.kv0, 0);
+  } else {
+    load_stage(it.kv0);
+    store_stage(0);
+  }
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const int tb = it.kv0 + t * kKvTile;
-    if (t + 1 < ntiles) load_stage(tb + kKvTile);
+    if (t + 1 < ntiles) {
+      if constexpr (B == kKvTile)
+        dma_stage(tb + kKvTile, (t + 1) & 1);
+      else
+        load_stage(tb + kKvTile);
+    }
     if (active) {
       const uint16_t* kt = lds + (t & 1) * L::STAGE;
       const uint16_t* vt = kt + L::KT;
@@ -504,6 +549,14 @@ __device__ void mfma_item(const AttnArgs& a, const ItemRec& it, uint16_t* lds) {
           sacc[h2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[kk], sacc[h2], 0, 0, 0);
         }
       }
+      // Schedule: the 16 K-fragment reads run four ahead of the 16 MFMAs
+      // (LDS reads 0x100, MFMA 0x008), so no MFMA waits on its own read.
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      for (int i = 0; i < 12; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       // raw scores; masked ones become -inf (only in boundary stages)
       float mt = -INFINITY;
       if (tb + kKvTile > it.kv1 || tb + kKvTile - 1 > lim_lo) {
@@ -572,7 +625,14 @@ __device__ void mfma_item(const AttnArgs& a, const ItemRec& it, uint16_t* lds) {
             o[dd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[h2][ks], o[dd], 0, 0, 0);
           }
     }
-    if (t + 1 < ntiles) store_stage((t + 1) & 1);
+    if (t + 1 < ntiles) {
+      if constexpr (B == kKvTile) {
+        __builtin_amdgcn_s_waitcnt(0);
+        fix_v_tail(tb + kKvTile, (t + 1) & 1);
+      } else {
+        store_stage((t + 1) & 1);
+      }
+    }
     __syncthreads();
   }
 
