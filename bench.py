@@ -211,6 +211,49 @@ def cpu_baseline(spec, tens, budget_s=30.0, min_s=10.0):
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
+def trace_cpu_baseline(passes, hq, hkv, d, bs, seed, wl, n_sample=8):
+    """The float64 oracle on a seeded sample of the trace's passes (append +
+    attention of each sampled pass, its sequences' histories regenerated from
+    the keyed generator and appended untimed).  Returns the mean per pass."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import attention as ora
+    rng = np.random.Generator(np.random.PCG64(seed + 1000))
+    picks = sorted(int(i) for i in rng.choice(len(passes), size=min(n_sample, len(passes)),
+                                               replace=False))
+    qh, kh = list(range(hq)), list(range(hkv))
+    times = []
+    for i in picks:
+        p = passes[i]
+        spec = wl.custom_spec("trace-cpu", p.q_lens, p.ctx_lens, hq, hkv, d, bs, seed=1, slack=1.0)
+        qs, kn, vn, hk, hv = [], [], [], [], []
+        for s in range(len(p.q_lens)):
+            rid, c, n = int(p.rids[s]), int(p.ctx_lens[s]), int(p.q_lens[s])
+            qs.append(wl.hash_normal_bf16(seed, wl.KIND_Q, rid, np.arange(c, c + n), qh, d))
+            k = wl.hash_normal_bf16(seed, wl.KIND_K, rid, np.arange(0, c + n), kh, d)
+            v = wl.hash_normal_bf16(seed, wl.KIND_V, rid, np.arange(0, c + n), kh, d)
+            hk.append(k[:c]); kn.append(k[c:]); hv.append(v[:c]); vn.append(v[c:])
+        kp, vp = wl.empty_pool_bits(spec)
+        hist = spec.history_pass()
+        if hist is not None:
+            kp, vp = ora.kv_append(kp, vp, hist[0], hist[1], hist[2], bs,
+                                   np.concatenate(hk), np.concatenate(hv))
+        t0 = time.perf_counter()
+        kp2, vp2 = ora.kv_append(kp, vp, spec.q_lens, spec.ctx_lens, spec.block_tables, bs,
+                                 np.concatenate(kn), np.concatenate(vn))
+        ora.attend(np.concatenate(qs), kp2, vp2, spec.q_lens, spec.ctx_lens, spec.block_tables,
+                   bs, hkv)
+        times.append(time.perf_counter() - t0)
+    blas = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
+    mean = float(np.mean(times))
+    return {"value": round(mean * 1e6, 1), "unit": "µs", "cores": int(max(blas) if blas else 1),
+            "kind": "oracle",
+            "sample": (f"{len(picks)} of {len(passes)} passes (seeded, {sum(times):.1f} s): append + "
+                       f"attention of every row of each; mean per pass; whole trace extrapolated "
+                       f"to {mean * len(passes):.0f} s"),
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
 def run_trace(args, torch, fgb, wl):
     """Replay the 512-request trace through the host SplitFuse scheduler.
 
@@ -319,6 +362,9 @@ def run_trace(args, torch, fgb, wl):
         },
     }
     keep.clear()
+    if not args.no_cpu:
+        res["cpu_baseline"] = trace_cpu_baseline(passes, hq, hkv, d, bs, seed, wl)
+        res["detail"]["gpu_vs_oracle"] = round(res["cpu_baseline"]["value"] / res["value"], 1)
     print(json.dumps(res), flush=True)
 
 
