@@ -15,7 +15,8 @@
  * Dynamic SplitKV Serving", section "3. Paged KV Memory Management with Zero
  * Overhead").  Long KV ranges are split over compute units and the partial
  * results merged by log-sum-exp (same page, section "1. Dynamic SplitKV
- * Attention").
+ * Attention"); the merge runs inside the attention launch, done by whichever
+ * work-group finishes a split group last.
  *
  * Call order for one pass, all on one HIP stream, nothing synchronises inside
  * the library:
@@ -63,7 +64,7 @@
 extern "C" {
 #endif
 
-#define FG_ABI_VERSION 2
+#define FG_ABI_VERSION 3
 
 typedef int32_t fg_status;
 
@@ -184,12 +185,16 @@ fg_status fg_upload_append(const fg_plan* plan, void* d_meta, const void* k_new,
 
 /* Attention of every query row of the pass over its sequence's cached keys
  * 0 .. ctx + j (inclusive causal bound), read through the block tables
- * (asynchronous).  The pools must already hold this pass's K/V (append
- * first, on the same stream).  q: [T, Hq, D] bf16.  out: [T, Hq, D] of
- * out_dtype (FG_DTYPE_F32 or FG_DTYPE_BF16).  lse: [T, Hq] fp32 or NULL.
+ * (asynchronous, one kernel launch).  The pools must already hold this pass's
+ * K/V (append first, on the same stream).  q: [T, Hq, D] bf16.  out: [T, Hq, D]
+ * of out_dtype (FG_DTYPE_F32 or FG_DTYPE_BF16).  lse: [T, Hq] fp32 or NULL.
  * d_ws: caller-owned workspace of >= workspace_bytes (may be NULL when that is
- * 0); its contents on entry do not matter. */
-fg_status fg_attention_ragged(const fg_plan* plan, const void* d_meta,
+ * 0); its contents on entry do not matter.
+ * d_meta is written as well as read: the split groups' arrival counters live
+ * in it.  They are zero after an upload and every call leaves them zero again,
+ * so one upload serves any number of calls; calls sharing one d_meta must not
+ * overlap in time (stream order them). */
+fg_status fg_attention_ragged(const fg_plan* plan, void* d_meta,
                               const void* q, const void* k_pool, const void* v_pool,
                               void* out, int32_t out_dtype, float* lse,
                               void* d_ws, size_t ws_bytes, void* stream);
@@ -211,15 +216,17 @@ int32_t fg_abi_version(void);
  *   sequence  8 ints: q_start, q_len, ctx, kv_len, block_id_offset, num_blocks, 0, 0
  *   block id  1 int:  physical block of each used table entry, per sequence
  *   run       4 ints: first new-token row, first slot, token count, block
- *   item      8 ints: seq, kv_head, row0, nrows, kv0, kv1, slot (-1 = final
- *                     rows, else first partial row), waves (0 = vector-ALU path)
- *   merge     8 ints: seq, kv_head, row0, nrows, nsplit, slot0, r_begin, r_count
+ *   item     12 ints: seq, kv_head, row0, nrows, kv0, kv1, slot (-1 = final
+ *                     rows, else first partial row), waves (0 = vector-ALU
+ *                     path), group (split group, -1 = unsplit), 0, 0, 0
+ *   merge     8 ints: seq, kv_head, row0, nrows, nsplit, slot0, 0, 0
+ *                     (one per split group)
+ *   counter   1 int:  arrival counter of each split group, 0
  * Packed row r of an item is query token r / G at q head kv_head * G + r % G;
- * split i of a split group's row r sits at partial row slot0 + i * nrows + r;
- * a merge record covers rows r_begin .. r_begin + r_count - 1 of its group.
+ * split i of a split group's row r sits at partial row slot0 + i * nrows + r.
  * host_dst may be NULL to query the layout only. */
 typedef struct fg_plan_layout_t {
-  int64_t seqs, block_ids, runs, items, merges;   /* byte offsets */
+  int64_t seqs, block_ids, runs, items, merges, counters;   /* byte offsets */
   int32_t num_seqs, num_block_ids, num_runs, num_items, num_merges, pad;
 } fg_plan_layout_t;
 
@@ -235,8 +242,7 @@ fg_status fg_plan_metadata(const fg_plan* plan, void* host_dst, size_t bytes,
 enum {
   FG_KERNEL_APPEND = 0,
   FG_KERNEL_ATTENTION = 1,
-  FG_KERNEL_MERGE = 2,
-  FG_KERNEL_COUNT = 3
+  FG_KERNEL_COUNT = 2
 };
 
 fg_status fg_profile_enable(int32_t on);

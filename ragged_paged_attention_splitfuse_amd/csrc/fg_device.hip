@@ -15,10 +15,14 @@
 //                   streams its own 32-token sub-tiles with 16-byte loads,
 //                   dot products on v_dot2_f32_bf16 with DPP row reductions, and
 //                   the four wavefronts merge by log-sum-exp at the end.
-//   merge_kernel    log-sum-exp merge of split partials ("DeepSpeed-FastGen
-//                   Guide: Dynamic SplitKV Serving", section "1. Dynamic SplitKV
-//                   Attention", two-phase softmax item; the weights are the
-//                   partials' log-sum-exp values).
+//                   An item that is one split of a longer KV range writes its
+//                   partial rows to the workspace and counts itself in on its
+//                   split group's counter; the work-group that completes the
+//                   count merges the group by log-sum-exp ("DeepSpeed-FastGen
+//                   Guide: Dynamic SplitKV Serving", section "1. Dynamic
+//                   SplitKV Attention", two-phase softmax item; the weights are
+//                   the partials' log-sum-exp values), so no merge launch
+//                   follows.
 //
 // Exponentials run base 2 on v_exp_f32 with the softmax scale folded into
 // scale * log2(e); log-sum-exp values are returned in natural-log units.
@@ -55,6 +59,8 @@ struct AttnArgs {
   const SeqRec* seqs;
   const int32_t* bt;
   const ItemRec* items;
+  const MergeRec* groups;   // split groups
+  int32_t* counters;        // one arrival counter per split group
   const uint16_t* q;
   const uint16_t* kpool;
   const uint16_t* vpool;
@@ -133,10 +139,19 @@ __device__ __forceinline__ void store_result(const AttnArgs& a, const SeqRec& sq
     }
     if (write_lse && a.lse) a.lse[idx] = lse_val;
   } else {
+    // Partial rows are written coherently at device scope (they are read by
+    // whichever work-group merges the split group, on any XCD), so no L2
+    // writeback is needed to publish them.
     float* o = a.ws_o + size_t(it.slot + r) * D + d0;
-    for (int e = 0; e < n; ++e) o[e] = vals[e];
-    if (write_lse) a.ws_lse[it.slot + r] = lse_val;
+    for (int e = 0; e < n; ++e) __hip_atomic_store(o + e, vals[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (write_lse)
+      __hip_atomic_store(a.ws_lse + it.slot + r, lse_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+}
+
+// Device-coherent read of a partial value (see the partial-row stores above).
+__device__ __forceinline__ float load_partial(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ----------------------------------------------------------------------------
@@ -662,6 +677,82 @@ constexpr int valu_lds_bytes() {
           kWaves * kValuMaxRows * D) * 4;
 }
 
+// Log-sum-exp merge of one split group (every row, every split), by the whole
+// work-group, all rows at once: first one thread per row finds the row's
+// largest partial lse and the sum of the weights e^(lse_i - max) and writes
+// the final lse = max + ln(sum); then every thread takes independent (row,
+// 4-dim) units and sums the weighted, normalised partial rows.  Same formula
+// as the pages' merge step.  `red` is LDS for 2 * nrows floats.  Partial
+// values are read with device-coherent loads.
+template <int D>
+__device__ void merge_group(const AttnArgs& a, const MergeRec& g, float* red) {
+  constexpr int CH = D / 4;
+  const int tid = threadIdx.x;
+  const SeqRec sq = a.seqs[g.seq];
+  ItemRec fin;
+  fin.seq = g.seq;
+  fin.kv_head = g.kv_head;
+  fin.row0 = g.row0;
+  fin.nrows = g.nrows;
+  fin.slot = -1;
+  for (int r = tid; r < g.nrows; r += kThreads) {
+    const float* ls = a.ws_lse + g.slot0 + r;
+    float mx = -INFINITY;
+    for (int i = 0; i < g.nsplit; ++i) mx = fmaxf(mx, load_partial(ls + size_t(i) * g.nrows));
+    float wsum = 0.f;
+    for (int i = 0; i < g.nsplit; ++i) {
+      const float li = load_partial(ls + size_t(i) * g.nrows);
+      wsum += (li == -INFINITY) ? 0.f : fast_exp2((li - mx) * kLog2e);
+    }
+    red[r] = mx;
+    red[g.nrows + r] = wsum > 0.f ? 1.f / wsum : 0.f;
+    store_result(a, sq, fin, D, r, 0, nullptr, 0, true,
+                 wsum > 0.f ? mx + fast_log2(wsum) * kLn2 : -INFINITY);
+  }
+  __syncthreads();
+  for (int u = tid; u < g.nrows * CH; u += kThreads) {
+    const int r = u / CH, c = u % CH;
+    const float mx = red[r], inv = red[g.nrows + r];
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < g.nsplit; ++i) {
+      const size_t pr = size_t(g.slot0) + size_t(i) * g.nrows + r;
+      const float li = load_partial(a.ws_lse + pr);
+      const float w = (li == -INFINITY) ? 0.f : fast_exp2((li - mx) * kLog2e) * inv;
+      const float* o = a.ws_o + pr * D + 4 * c;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = fmaf(w, load_partial(o + e), acc[e]);
+    }
+    store_result(a, sq, fin, D, r, 4 * c, acc, 4, false, 0.f);
+  }
+}
+
+// End of a split item: its partial rows are in the workspace, written with
+// device-coherent stores.  Wait until they have completed, count the split in
+// with one device-scope atomic, and if this work-group brought the count to
+// nsplit, merge the group (device-coherent loads see every split's rows: each
+// split's stores completed before its count) and re-arm the counter for the
+// next call.  Counters start at zero (the uploaded metadata holds zeros).  No
+// whole-cache writeback or invalidation is involved, so the KV that other
+// work-groups keep in L2 stays there.
+// `last_flag` is the first word of the item's LDS (the merge uses the LDS
+// from 16 bytes on); the barrier before thread 0 writes it follows every LDS
+// access of the item.
+template <int D>
+__device__ void finish_split(const AttnArgs& a, const ItemRec& it, int* last_flag) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int prev = __hip_atomic_fetch_add(a.counters + it.group, 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+    *last_flag = prev == a.groups[it.group].nsplit - 1;
+  }
+  __syncthreads();
+  if (!*last_flag) return;
+  merge_group<D>(a, a.groups[it.group], reinterpret_cast<float*>(last_flag) + 4);
+  if (threadIdx.x == 0)
+    __hip_atomic_store(a.counters + it.group, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int D, int B, bool MFMA>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   constexpr int kLds = MFMA ? (MfmaLds<D>::BYTES > valu_lds_bytes<D>() ? MfmaLds<D>::BYTES
@@ -672,6 +763,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   if constexpr (MFMA) {
     if (it.waves > 0) {
       mfma_item<D, B>(a, it, reinterpret_cast<uint16_t*>(smem));
+      if (it.group >= 0) finish_split<D>(a, it, reinterpret_cast<int*>(smem));
       return;
     }
   }
@@ -679,42 +771,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
     valu_item<D, B, 1>(a, it, reinterpret_cast<float*>(smem));
   else
     valu_item<D, B, kValuMaxRows>(a, it, reinterpret_cast<float*>(smem));
-}
-
-// One wavefront per merged row; lane holds D/64 consecutive dims.
-template <int D>
-__global__ __launch_bounds__(kThreads) void merge_kernel(AttnArgs a, const MergeRec* merges) {
-  constexpr int PL = D / 64;
-  const MergeRec mg = merges[blockIdx.x];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (wave >= mg.r_count) return;
-  const int r = mg.r_begin + wave;
-  float mx = -INFINITY;
-  for (int i = 0; i < mg.nsplit; ++i) mx = fmaxf(mx, a.ws_lse[mg.slot0 + i * mg.nrows + r]);
-  float wsum = 0.f, acc[PL];
-#pragma unroll
-  for (int e = 0; e < PL; ++e) acc[e] = 0.f;
-#pragma unroll 4
-  for (int i = 0; i < mg.nsplit; ++i) {
-    const int pr = mg.slot0 + i * mg.nrows + r;
-    const float li = a.ws_lse[pr];
-    const float w = (li == -INFINITY) ? 0.f : fast_exp2((li - mx) * kLog2e);
-    wsum += w;
-    const float* src = a.ws_o + size_t(pr) * D + PL * lane;
-#pragma unroll
-    for (int e = 0; e < PL; ++e) acc[e] = fmaf(w, src[e], acc[e]);
-  }
-  const float inv = 1.f / wsum;
-#pragma unroll
-  for (int e = 0; e < PL; ++e) acc[e] *= inv;
-  const SeqRec sq = a.seqs[mg.seq];
-  ItemRec it;
-  it.seq = mg.seq;
-  it.kv_head = mg.kv_head;
-  it.row0 = mg.row0;
-  it.nrows = mg.nrows;
-  it.slot = -1;
-  store_result(a, sq, it, D, r, PL * lane, acc, PL, lane == 0, mx + fast_log2(wsum) * kLn2);
+  if (it.group >= 0) finish_split<D>(a, it, reinterpret_cast<int*>(smem));
 }
 
 // Append of one run (up to B consecutive new tokens of one sequence in one
@@ -1016,7 +1073,7 @@ extern "C" fg_status fg_upload_append(const fg_plan* plan, void* d_meta, const v
   return fg_kv_append(plan, d_meta, k_new, v_new, k_pool, v_pool, stream);
 }
 
-extern "C" fg_status fg_attention_ragged(const fg_plan* plan, const void* d_meta, const void* q,
+extern "C" fg_status fg_attention_ragged(const fg_plan* plan, void* d_meta, const void* q,
                                          const void* k_pool, const void* v_pool, void* out,
                                          int32_t out_dtype, float* lse, void* d_ws,
                                          size_t ws_bytes, void* stream) {
@@ -1030,11 +1087,13 @@ extern "C" fg_status fg_attention_ragged(const fg_plan* plan, const void* d_meta
   if (plan->ws_bytes > 0 && (!d_ws || ws_bytes < plan->ws_bytes || !aligned16(d_ws)))
     return FG_E_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const uint8_t* meta = static_cast<const uint8_t*>(d_meta);
+  uint8_t* meta = static_cast<uint8_t*>(d_meta);
   AttnArgs a;
   a.seqs = reinterpret_cast<const SeqRec*>(meta + plan->off_seqs);
   a.bt = reinterpret_cast<const int32_t*>(meta + plan->off_bt);
   a.items = reinterpret_cast<const ItemRec*>(meta + plan->off_items);
+  a.groups = reinterpret_cast<const MergeRec*>(meta + plan->off_merges);
+  a.counters = reinterpret_cast<int32_t*>(meta + plan->off_counters);
   a.q = static_cast<const uint16_t*>(q);
   a.kpool = static_cast<const uint16_t*>(k_pool);
   a.vpool = static_cast<const uint16_t*>(v_pool);
@@ -1061,16 +1120,6 @@ extern "C" fg_status fg_attention_ragged(const fg_plan* plan, const void* d_meta
   } while (0)
     FG_SWITCH_DB(plan->head_dim, plan->block_size, FG_LAUNCH_ATTN);
 #undef FG_LAUNCH_ATTN
-    if (hipGetLastError() != hipSuccess) return FG_E_HIP;
-  }
-  if (plan->n_merge > 0) {
-    ProfScope prof(FG_KERNEL_MERGE, s);
-    const MergeRec* merges = reinterpret_cast<const MergeRec*>(meta + plan->off_merges);
-    const dim3 grid(unsigned(plan->n_merge));
-    if (plan->head_dim == 64)
-      hipLaunchKernelGGL((merge_kernel<64>), grid, dim3(kThreads), 0, s, a, merges);
-    else
-      hipLaunchKernelGGL((merge_kernel<128>), grid, dim3(kThreads), 0, s, a, merges);
     if (hipGetLastError() != hipSuccess) return FG_E_HIP;
   }
   return FG_OK;
@@ -1110,7 +1159,6 @@ extern "C" const char* fg_kernel_name(int32_t id) {
   switch (id) {
     case FG_KERNEL_APPEND: return "append_kernel";
     case FG_KERNEL_ATTENTION: return "attn_kernel";
-    case FG_KERNEL_MERGE: return "merge_kernel";
     default: return "unknown";
   }
 }

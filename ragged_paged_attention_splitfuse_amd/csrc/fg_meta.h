@@ -51,13 +51,15 @@ struct ItemRec {
   int32_t kv1;
   int32_t slot;      // -1: write final out/lse; else first partial row
   int32_t waves;     // matrix-core path: active wavefronts (1..4); else 0
+  int32_t group;     // split group (index into the group records), -1 if unsplit
+  int32_t pad0, pad1, pad2;
 };
 
-// Rows of a split group: the group has `nsplit` partials of `nrows` rows each,
-// split i of row r at partial row slot0 + i * nrows + r.  One record covers
-// rows [r_begin, r_begin + r_count) of the group, r_count <= kMergeRowsPerRec
-// (one wavefront per row).
-constexpr int kMergeRowsPerRec = 4;
+// A split group: the rows of one item-row range whose KV range was cut into
+// `nsplit` items.  Split i of row r writes partial row slot0 + i * nrows + r;
+// the work-group that finishes the group's last split merges all of them.
+// Each group owns one int32 arrival counter in the counter section (zero on
+// upload, reset to zero by the merging work-group).
 struct MergeRec {
   int32_t seq;
   int32_t kv_head;
@@ -65,13 +67,12 @@ struct MergeRec {
   int32_t nrows;
   int32_t nsplit;
   int32_t slot0;
-  int32_t r_begin;
-  int32_t r_count;
+  int32_t pad0, pad1;
 };
 
 static_assert(sizeof(SeqRec) == 32, "SeqRec layout");
 static_assert(sizeof(RunRec) == 16, "RunRec layout");
-static_assert(sizeof(ItemRec) == 32, "ItemRec layout");
+static_assert(sizeof(ItemRec) == 48, "ItemRec layout");
 static_assert(sizeof(MergeRec) == 32, "MergeRec layout");
 
 }  // namespace fg

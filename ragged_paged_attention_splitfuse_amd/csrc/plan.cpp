@@ -6,7 +6,8 @@
 // grouped (few rows -> vector-ALU items, many rows -> 128-row matrix-core
 // tiles), and each group's visible KV range is split over compute units when
 // it is long compared with the pass's total work.  Split partials are merged
-// by log-sum-exp afterwards.
+// by log-sum-exp inside the attention launch: the work-group that finishes a
+// split group's last split merges it.
 //
 // The length-aware split follows the adaptive split-KV idea of "DeepSpeed-
 // FastGen Guide: Dynamic SplitKV Serving" (section "1. Dynamic SplitKV
@@ -39,17 +40,20 @@ constexpr int kMaxSplitsLimit = 256;
 // Items longer than total / (CUs * kItemsPerCu) are split.  Two per CU (one
 // per resident work-group slot) is enough for longest-first dispatch to end
 // with every CU busy until close to the mean; a finer target buys little
-// balance and costs partial-row traffic plus a merge launch (measured on the
-// 7B 2048-token pass: 256 us per pass at 2, 280 us at 3 and 4).
+// balance and costs partial-row traffic plus the merge (measured on the 7B
+// 2048-token pass: 256 us per pass at 2, 280 us at 3 and 4).
 constexpr double kItemsPerCu = 2.0;
 // Matrix-core tiles: relative cost per KV token of a tile with R padded rows
 // is max(kMfmaMinCost, R / kFlopPerByte), where kFlopPerByte is the ratio of
 // achievable bf16 MFMA rate to achievable HBM rate on MI355X (about
 // 1000 TFLOP/s : 6 TB/s).  Splitting a prefill tile (two or more wavefronts)
 // buys no attention time once there are at least as many tiles as CUs, but
-// moves its partial rows through the workspace and adds the merge, so such
-// tiles are split only when they are too few to occupy the CUs (then to about
-// kMfmaSlotsPerCu items per CU, never below kMfmaMinSplitTokens).  One-wave
+// moves its partial rows through the workspace and puts the merge on the
+// group's last split, so such tiles are split only when they are too few to
+// occupy the CUs (then to about kMfmaSlotsPerCu items per CU, never below
+// kMfmaMinSplitTokens).  Measured on MI355X: splitting tiles longer than
+// 1.5x the per-slot mean slowed the 70B-class chunk pass from 99 to 113 us,
+// and 1.0x slowed the 7B chunk from 107 to 168 us.  One-wave
 // groups (GQA decodes) are bandwidth-bound like decodes and use the common
 // target.
 constexpr double kFlopPerByte = 170.0;
@@ -291,7 +295,6 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
     valu.reserve(groups.size() * 2);
     std::vector<MergeRec> merges;
     int64_t partial_rows = 0;
-    int32_t merge_groups = 0;
     int max_used = 1;
     int32_t order = 0;
     for (const Group& grp : groups) {
@@ -312,23 +315,21 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
       k = ceil_div(grp.vis_end, chunk);
       max_used = std::max<int>(max_used, int(k));
       int32_t slot0 = -1;
+      int32_t group = -1;
       if (k > 1) {
         if (partial_rows + k * grp.nrows > INT32_MAX) return FG_E_RANGE;
         slot0 = int32_t(partial_rows);
         partial_rows += k * grp.nrows;
-        ++merge_groups;
-        for (int rb = 0; rb < grp.nrows; rb += fg::kMergeRowsPerRec) {
-          MergeRec m;
-          m.seq = grp.seq;
-          m.kv_head = grp.kv_head;
-          m.row0 = grp.row0;
-          m.nrows = grp.nrows;
-          m.nsplit = int32_t(k);
-          m.slot0 = slot0;
-          m.r_begin = rb;
-          m.r_count = std::min(fg::kMergeRowsPerRec, grp.nrows - rb);
-          merges.push_back(m);
-        }
+        group = int32_t(merges.size());
+        MergeRec m;
+        m.seq = grp.seq;
+        m.kv_head = grp.kv_head;
+        m.row0 = grp.row0;
+        m.nrows = grp.nrows;
+        m.nsplit = int32_t(k);
+        m.slot0 = slot0;
+        m.pad0 = m.pad1 = 0;
+        merges.push_back(m);
       }
       for (int64_t i = 0; i < k; ++i) {
         Pending p;
@@ -340,6 +341,8 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
         p.item.kv1 = int32_t(std::min<int64_t>(grp.vis_end, (i + 1) * chunk));
         p.item.slot = k > 1 ? int32_t(slot0 + i * grp.nrows) : -1;
         p.item.waves = grp.waves;
+        p.item.group = group;
+        p.item.pad0 = p.item.pad1 = p.item.pad2 = 0;
         p.cost = double(p.item.kv1 - p.item.kv0) * (grp.cost / double(grp.vis_end));
         p.order = order++;
         (grp.waves ? mfma : valu).push_back(p);
@@ -369,8 +372,7 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
     plan->n_mfma = int32_t(mfma.size());
     plan->n_valu = int32_t(valu.size());
     plan->n_items = plan->n_mfma + plan->n_valu;
-    plan->n_merge = int32_t(merges.size());
-    plan->n_merge_groups = merge_groups;
+    plan->n_merge_groups = int32_t(merges.size());
     plan->n_partial_rows = int32_t(partial_rows);
     plan->max_splits_used = max_used;
     plan->target_cus = target_cus;
@@ -381,6 +383,7 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
     plan->off_runs = off;   off = align16(off + sizeof(RunRec) * runs.size());
     plan->off_items = off;  off = align16(off + sizeof(ItemRec) * size_t(plan->n_items));
     plan->off_merges = off; off = align16(off + sizeof(MergeRec) * merges.size());
+    plan->off_counters = off; off = align16(off + sizeof(int32_t) * merges.size());
     plan->blob.assign(std::max<size_t>(off, 16), 0);
     uint8_t* base = plan->blob.data();
     if (!seqs.empty()) memcpy(base + plan->off_seqs, seqs.data(), sizeof(SeqRec) * seqs.size());
@@ -450,11 +453,12 @@ extern "C" fg_status fg_plan_metadata(const fg_plan* p, void* host_dst, size_t b
     layout->runs = int64_t(p->off_runs);
     layout->items = int64_t(p->off_items);
     layout->merges = int64_t(p->off_merges);
+    layout->counters = int64_t(p->off_counters);
     layout->num_seqs = p->num_seqs;
     layout->num_block_ids = int32_t((p->off_runs - p->off_bt) / sizeof(int32_t));
     layout->num_runs = p->n_runs;
     layout->num_items = p->n_items;
-    layout->num_merges = p->n_merge;
+    layout->num_merges = p->n_merge_groups;
   }
   return FG_OK;
 }

@@ -16,17 +16,17 @@ struct fg_plan {
   int32_t hq = 0, hkv = 0, group = 0, head_dim = 0, block_size = 0, num_blocks = 0;
   float scale = 0.f;
 
-  // Packed device metadata: [SeqRec][block ids][RunRec][ItemRec][MergeRec],
-  // each section starting on a 16-byte boundary (byte offsets below).
+  // Packed device metadata: [SeqRec][block ids][RunRec][ItemRec][MergeRec]
+  // [int32 split-group counters, zero], each section starting on a 16-byte
+  // boundary (byte offsets below).
   std::vector<uint8_t> blob;
-  size_t off_seqs = 0, off_bt = 0, off_runs = 0, off_items = 0, off_merges = 0;
+  size_t off_seqs = 0, off_bt = 0, off_runs = 0, off_items = 0, off_merges = 0, off_counters = 0;
 
   int32_t n_runs = 0;
   int32_t n_items = 0;   // n_mfma matrix-core items first, then n_valu
   int32_t n_mfma = 0;
   int32_t n_valu = 0;
-  int32_t n_merge = 0;          // merge records (<= kMergeRowsPerRec rows each)
-  int32_t n_merge_groups = 0;   // row groups that were split
+  int32_t n_merge_groups = 0;   // row groups that were split (one MergeRec each)
   int32_t n_partial_rows = 0;
   int32_t max_splits_used = 0;
   int32_t target_cus = 0;

@@ -3,8 +3,9 @@
 A plan is correct when, for every query row (s, j, h), the KV ranges of the
 items that compute it partition [0, ctx + j] (plus at most the few keys past
 a row's causal limit inside its tile, which the kernels mask), split partials
-land in disjoint workspace rows named by one merge group, and every new token
-is appended to exactly the slot its block table names.
+land in disjoint workspace rows named by one split group (whose record and
+zeroed arrival counter every split item points at), and every new token is
+appended to exactly the slot its block table names.
 """
 from collections import defaultdict
 
@@ -31,27 +32,29 @@ def check_plan(plan, spec):
         q_start += q
 
     # items: path, alignment, grouping
+    assert items.shape[1] == 12
     groups = defaultdict(list)
     for idx, it in enumerate(items):
-        seq, kvh, row0, nrows, kv0, kv1, slot, waves = map(int, it)
+        seq, kvh, row0, nrows, kv0, kv1, slot, waves, grp = map(int, it[:9])
+        assert not it[9:].any()
         assert 0 <= seq < spec.num_seqs and 0 <= kvh < spec.num_kv_heads
         assert nrows >= 1 and kv1 > kv0 >= 0 and kv0 % 64 == 0
         if waves > 0:
             assert waves == -(-nrows // 32) and nrows <= 128
         else:
             assert nrows <= 4
-        groups[(seq, kvh, row0, nrows)].append((kv0, kv1, slot))
+        assert (slot < 0) == (grp < 0) and -1 <= grp < len(merges)
+        groups[(seq, kvh, row0, nrows)].append((kv0, kv1, slot, grp))
 
+    # one record and one zeroed counter per split group
+    assert len(meta["counters"]) == len(merges) and not meta["counters"].any()
     merge_by_group = {}
-    merge_rows = defaultdict(list)
-    for m in merges:
-        seq, kvh, row0, nrows, nsplit, slot0, r_begin, r_count = map(int, m)
+    for gi, m in enumerate(merges):
+        seq, kvh, row0, nrows, nsplit, slot0, pad0, pad1 = map(int, m)
+        assert pad0 == 0 and pad1 == 0 and nsplit >= 2
         key = (seq, kvh, row0, nrows)
-        assert merge_by_group.setdefault(key, (nsplit, slot0)) == (nsplit, slot0)
-        assert 1 <= r_count <= 4 and 0 <= r_begin and r_begin + r_count <= nrows
-        merge_rows[key].extend(range(r_begin, r_begin + r_count))
-    for key, rows in merge_rows.items():
-        assert sorted(rows) == list(range(key[3]))
+        assert key not in merge_by_group
+        merge_by_group[key] = (nsplit, slot0, gi)
 
     used_slots = np.zeros(info["num_partial_rows"], dtype=np.int32)
     rows_seen = defaultdict(int)
@@ -60,15 +63,15 @@ def check_plan(plan, spec):
         c = int(spec.ctx_lens[seq])
         vis_end = c + (row0 + nrows - 1) // g_ratio + 1
         assert parts[0][0] == 0 and parts[-1][1] == vis_end
-        for (a0, a1, _), (b0, b1, _) in zip(parts, parts[1:]):
+        for (a0, a1, _, _), (b0, b1, _, _) in zip(parts, parts[1:]):
             assert a1 == b0
         if len(parts) == 1:
             assert parts[0][2] == -1 and (seq, kvh, row0, nrows) not in merge_by_group
         else:
-            nsplit, slot0 = merge_by_group[(seq, kvh, row0, nrows)]
+            nsplit, slot0, gi = merge_by_group[(seq, kvh, row0, nrows)]
             assert nsplit == len(parts)
-            for i, (_, _, slot) in enumerate(parts):
-                assert slot == slot0 + i * nrows
+            for i, (_, _, slot, grp) in enumerate(parts):
+                assert slot == slot0 + i * nrows and grp == gi
                 used_slots[slot:slot + nrows] += 1
         for r in range(row0, row0 + nrows):
             rows_seen[(seq, kvh, r)] += 1

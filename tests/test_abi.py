@@ -35,7 +35,7 @@ def test_binding_covers_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert binding.fg_abi_version() == 2
+    assert binding.fg_abi_version() == 3
     assert binding.status_string(0) == "ok"
     assert "twice" in binding.status_string(binding.FG_E_ALIAS)
     assert binding.status_string(12345) == "unknown status"
@@ -49,7 +49,8 @@ def test_struct_sizes_match_header_layout(tmp_path):
     cc = shutil.which("gcc") or shutil.which("cc")
     if cc is None:
         pytest.skip("no host C compiler")
-    structs = {"fg_pass_desc": binding.fg_pass_desc, "fg_plan_info_t": binding.fg_plan_info_t}
+    structs = {"fg_pass_desc": binding.fg_pass_desc, "fg_plan_info_t": binding.fg_plan_info_t,
+               "fg_plan_layout_t": binding.fg_plan_layout_t}
     lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "fg.h"', "int main(void) {"]
     for name, cls in structs.items():
         lines.append(f'  printf("{name} %zu\\n", sizeof({name}));')

@@ -5,6 +5,7 @@ Bars: KV append and block addressing bit-exact; attention max-abs error
 Inputs are the seeded generator's; pools start poisoned with bf16 NaN so that
 any read of an unwritten slot shows up.
 """
+import ctypes
 import math
 
 import numpy as np
@@ -147,6 +148,55 @@ def test_forced_splits_gqa_tiles():
     assert plan.info["num_merge_groups"] > 0
     o_ref, l_ref = G.oracle_pass(spec, tens)
     compare(out, lse, o_ref, l_ref, "gqa tiles force_splits=5")
+
+
+@pytest.mark.parametrize("name,splits", [("gqa8_d128_b64_mixed", 7), ("mha_d64_b32_mixed", 5),
+                                         ("over64", 100)])
+def test_split_groups_merge_in_launch_and_rearm(name, splits):
+    # Split items merge inside the attention launch: the last split of a group
+    # to finish merges it and re-arms the group's counter.  Three launches on
+    # one upload must agree bit for bit, match the oracle, and leave every
+    # counter at zero.  "over64" has a decode split 71 ways (the merge reads
+    # split lse values 64 lanes at a time).
+    if name == "over64":
+        spec = wl.custom_spec("over64", [1, 1, 20], [9000, 300, 700], 8, 2, 128, 64, seed=27)
+    else:
+        spec = SMALL_SPECS[name]()
+    _log(f"[case] in-launch merge {name} force_splits={splits}")
+    tens = wl.make_tensors(spec)
+    kp, vp = G.gpu_pools(spec)
+    G.fill_history(spec, tens, kp, vp)
+    plan = fgb.Plan.from_spec(spec, force_splits=splits, target_cus=16)
+    check_plan(plan, spec)
+    assert plan.info["num_merge_groups"] > 0
+    if name == "over64":
+        assert plan.info["max_splits_used"] > 64
+    meta = plan.upload()
+    q, kn, vn = G.to_dev(tens.q), G.to_dev(tens.k_new), G.to_dev(tens.v_new)
+    fgb.kv_append(plan, meta, kn, vn, kp, vp)
+    t, hq, d = spec.num_tokens, spec.num_q_heads, spec.head_dim
+    runs = []
+    for _ in range(3):
+        out = torch.full((t, hq, d), float("nan"), dtype=torch.float32, device="cuda")
+        lse = torch.full((t, hq), float("nan"), dtype=torch.float32, device="cuda")
+        fgb.attention_ragged(plan, meta, q, kp, vp, out, lse)
+        torch.cuda.synchronize()
+        runs.append((out, lse))
+    for out, lse in runs[1:]:
+        assert torch.equal(out, runs[0][0]) and torch.equal(lse, runs[0][1])
+    raw = meta.cpu().numpy()[:plan.info["metadata_bytes"]].view(np.int32)
+    words = plan.info["num_merge_groups"]
+    start = plan_counter_offset(plan) // 4
+    counters = raw[start:start + words]
+    assert words == plan.info["num_merge_groups"] and not counters.any()
+    o_ref, l_ref = G.oracle_pass(spec, tens)
+    compare(runs[0][0], runs[0][1], o_ref, l_ref, f"in-launch merge {name}")
+
+
+def plan_counter_offset(plan):
+    lay = fgb.fg_plan_layout_t()
+    fgb._check(fgb.lib().fg_plan_metadata(plan.handle, None, 0, ctypes.byref(lay)), "fg_plan_metadata")
+    return int(lay.counters)
 
 
 def test_block_permutation_is_bit_identical():
