@@ -441,7 +441,7 @@ def measure_pass(torch, fgb, spec, tens, dev, stream, knobs, steps, warmup, sepa
 
 def kernel_us(kern):
     out = {}
-    for key, name in (("append", "append_kernel"), ("attention", "attn_kernel")):
+    for key, name in (("append", "append_kernel"), ("attention", "attn_kernel"), ("merge", "merge_kernel")):
         ms, n = kern[name]
         out[key] = ms * 1e3 / n if n else 0.0
     return out
@@ -579,8 +579,10 @@ def main():
 
     attn_ms, attn_n = kern["attn_kernel"]
     app_ms, app_n = kern["append_kernel"]
+    mrg_ms, mrg_n = kern["merge_kernel"]
     attn_us = attn_ms * 1e3 / max(1, attn_n)
     app_us = app_ms * 1e3 / max(1, app_n)
+    mrg_us = mrg_ms * 1e3 / max(1, mrg_n) if mrg_n else 0.0
     attn_gbs = alg["attn_bytes"] / (attn_us * 1e-6) / 1e9
     attn_tflops = alg["flops"] / (attn_us * 1e-6) / 1e12
     pass_us = ms_per_step * 1e3
@@ -627,7 +629,8 @@ def main():
         "cpu_baseline": None,
         "detail": {
             "tokens_per_s": round(t / (pass_us * 1e-6), 1),
-            "kernel_us": {"append": round(app_us, 2), "attention": round(attn_us, 2)},
+            "kernel_us": {"append": round(app_us, 2), "attention": round(attn_us, 2),
+                          "merge": round(mrg_us, 2)},
             "attn_gbs": round(attn_gbs, 1), "attn_hbm_frac": round(attn_gbs / PEAK_HBM_GBS, 4),
             "attn_tflops": round(attn_tflops, 2),
             "attn_mfma_frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
@@ -639,7 +642,8 @@ def main():
                              "median": round(float(np.median(cold)), 2),
                              "p90": round(float(np.percentile(cold, 90)), 2)} if cold else None,
             "plan": {k: info[k] for k in ("num_items", "num_valu_items", "num_mfma_items",
-                                          "num_merge_groups", "max_splits_used", "target_cus")},
+                                          "num_merge_groups", "num_inlaunch_merge_groups", "max_splits_used",
+                                          "target_cus")},
             "algorithmic": alg,
             "achievable": achievable,
             "attn_frac_of_achievable": {

@@ -15,8 +15,9 @@
  * Dynamic SplitKV Serving", section "3. Paged KV Memory Management with Zero
  * Overhead").  Long KV ranges are split over compute units and the partial
  * results merged by log-sum-exp (same page, section "1. Dynamic SplitKV
- * Attention"); the merge runs inside the attention launch, done by whichever
- * work-group finishes a split group last.
+ * Attention"); for decode rows the merge runs inside the attention launch,
+ * done by whichever work-group finishes a split group last, and split prefill
+ * tiles are merged by a short launch after it.
  *
  * Call order for one pass, all on one HIP stream, nothing synchronises inside
  * the library:
@@ -146,6 +147,8 @@ typedef struct fg_plan_info_t {
   int32_t max_splits_used;
   int32_t num_append_runs; /* (sequence, block) runs the append writes */
   int32_t target_cus;      /* CU count the plan was balanced for */
+  int32_t num_inlaunch_merge_groups; /* split groups merged inside the attention
+                              launch (the rest get a merge launch after it) */
 } fg_plan_info_t;
 
 /* Build the plan of one pass (host only, no device call unless
@@ -185,7 +188,8 @@ fg_status fg_upload_append(const fg_plan* plan, void* d_meta, const void* k_new,
 
 /* Attention of every query row of the pass over its sequence's cached keys
  * 0 .. ctx + j (inclusive causal bound), read through the block tables
- * (asynchronous, one kernel launch).  The pools must already hold this pass's
+ * (asynchronous; one kernel launch, plus a merge launch when the plan splits
+ * prefill tiles).  The pools must already hold this pass's
  * K/V (append first, on the same stream).  q: [T, Hq, D] bf16.  out: [T, Hq, D]
  * of out_dtype (FG_DTYPE_F32 or FG_DTYPE_BF16).  lse: [T, Hq] fp32 or NULL.
  * d_ws: caller-owned workspace of >= workspace_bytes (may be NULL when that is
@@ -220,14 +224,16 @@ int32_t fg_abi_version(void);
  *                     rows, else first partial row), waves (0 = vector-ALU
  *                     path), group (split group, -1 = unsplit), 0, 0, 0
  *   merge     8 ints: seq, kv_head, row0, nrows, nsplit, slot0, 0, 0
- *                     (one per split group)
- *   counter   1 int:  arrival counter of each split group, 0
+ *                     (one per split group; the first num_counters groups are
+ *                     merged inside the attention launch, the rest by a merge
+ *                     launch after it)
+ *   counter   1 int:  arrival counter of each in-launch split group, 0
  * Packed row r of an item is query token r / G at q head kv_head * G + r % G;
  * split i of a split group's row r sits at partial row slot0 + i * nrows + r.
  * host_dst may be NULL to query the layout only. */
 typedef struct fg_plan_layout_t {
   int64_t seqs, block_ids, runs, items, merges, counters;   /* byte offsets */
-  int32_t num_seqs, num_block_ids, num_runs, num_items, num_merges, pad;
+  int32_t num_seqs, num_block_ids, num_runs, num_items, num_merges, num_counters;
 } fg_plan_layout_t;
 
 fg_status fg_plan_metadata(const fg_plan* plan, void* host_dst, size_t bytes,
@@ -242,7 +248,8 @@ fg_status fg_plan_metadata(const fg_plan* plan, void* host_dst, size_t bytes,
 enum {
   FG_KERNEL_APPEND = 0,
   FG_KERNEL_ATTENTION = 1,
-  FG_KERNEL_COUNT = 2
+  FG_KERNEL_MERGE = 2,
+  FG_KERNEL_COUNT = 3
 };
 
 fg_status fg_profile_enable(int32_t on);

@@ -22,7 +22,7 @@ FG_E_INVALID, FG_E_RANGE, FG_E_ALIAS, FG_E_UNSUPPORTED = -1, -2, -3, -4
 FG_E_WORKSPACE, FG_E_HIP, FG_E_NOMEM = -5, -6, -7
 FG_DTYPE_F32, FG_DTYPE_BF16 = 0, 1
 FG_SPLIT_BALANCED, FG_SPLIT_ENGINE, FG_SPLIT_PER_1K = 0, 1, 2
-FG_KERNEL_APPEND, FG_KERNEL_ATTENTION, FG_KERNEL_COUNT = 0, 1, 2
+FG_KERNEL_APPEND, FG_KERNEL_ATTENTION, FG_KERNEL_MERGE, FG_KERNEL_COUNT = 0, 1, 2, 3
 
 _I32P = ctypes.POINTER(ctypes.c_int32)
 
@@ -53,7 +53,7 @@ class fg_plan_info_t(ctypes.Structure):
         ("num_valu_items", ctypes.c_int32), ("num_mfma_items", ctypes.c_int32),
         ("num_merge_groups", ctypes.c_int32), ("num_partial_rows", ctypes.c_int32),
         ("max_splits_used", ctypes.c_int32), ("num_append_runs", ctypes.c_int32),
-        ("target_cus", ctypes.c_int32),
+        ("target_cus", ctypes.c_int32), ("num_inlaunch_merge_groups", ctypes.c_int32),
     ]
 
 
@@ -63,7 +63,7 @@ class fg_plan_layout_t(ctypes.Structure):
         ("items", ctypes.c_int64), ("merges", ctypes.c_int64), ("counters", ctypes.c_int64),
         ("num_seqs", ctypes.c_int32), ("num_block_ids", ctypes.c_int32),
         ("num_runs", ctypes.c_int32), ("num_items", ctypes.c_int32),
-        ("num_merges", ctypes.c_int32), ("pad", ctypes.c_int32),
+        ("num_merges", ctypes.c_int32), ("num_counters", ctypes.c_int32),
     ]
 
 
@@ -209,7 +209,7 @@ class Plan:
             "runs": section(lay.runs, lay.num_runs, 4),
             "items": section(lay.items, lay.num_items, 12),
             "merges": section(lay.merges, lay.num_merges, 8),
-            "counters": words[lay.counters // 4: lay.counters // 4 + lay.num_merges].copy(),
+            "counters": words[lay.counters // 4: lay.counters // 4 + lay.num_counters].copy(),
             "raw": buf[:nbytes].copy(),
         }
 

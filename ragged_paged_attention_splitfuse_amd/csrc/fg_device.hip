@@ -21,8 +21,10 @@
 //                   count merges the group by log-sum-exp ("DeepSpeed-FastGen
 //                   Guide: Dynamic SplitKV Serving", section "1. Dynamic
 //                   SplitKV Attention", two-phase softmax item; the weights are
-//                   the partials' log-sum-exp values), so no merge launch
-//                   follows.
+//                   the partials' log-sum-exp values).  This is done for
+//                   groups of up to one wavefront's rows (decodes).
+//   merge_kernel    the same merge for split prefill tiles, one work-group per
+//                   group, after the attention launch.
 //
 // Exponentials run base 2 on v_exp_f32 with the softmax scale folded into
 // scale * log2(e); log-sum-exp values are returned in natural-log units.
@@ -59,8 +61,8 @@ struct AttnArgs {
   const SeqRec* seqs;
   const int32_t* bt;
   const ItemRec* items;
-  const MergeRec* groups;   // split groups
-  int32_t* counters;        // one arrival counter per split group
+  const MergeRec* groups;   // split groups (in-launch ones first)
+  int32_t* counters;        // one arrival counter per in-launch split group
   const uint16_t* q;
   const uint16_t* kpool;
   const uint16_t* vpool;
@@ -69,6 +71,7 @@ struct AttnArgs {
   float* ws_o;
   float* ws_lse;
   int32_t hq, hkv, group, n_mfma;
+  int32_t n_inlaunch;       // split groups merged inside the attention launch
   float scale_log2;  // softmax scale * log2(e)
   int32_t out_bf16;
 };
@@ -138,20 +141,28 @@ __device__ __forceinline__ void store_result(const AttnArgs& a, const SeqRec& sq
       for (int e = 0; e < n; ++e) o[e] = vals[e];
     }
     if (write_lse && a.lse) a.lse[idx] = lse_val;
-  } else {
-    // Partial rows are written coherently at device scope (they are read by
-    // whichever work-group merges the split group, on any XCD), so no L2
-    // writeback is needed to publish them.
+  } else if (it.group < a.n_inlaunch) {
+    // Partial rows of an in-launch group are written coherently at device
+    // scope (whichever work-group merges the group reads them, on any XCD),
+    // so no L2 write-back is needed to publish them.
     float* o = a.ws_o + size_t(it.slot + r) * D + d0;
     for (int e = 0; e < n; ++e) __hip_atomic_store(o + e, vals[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (write_lse)
       __hip_atomic_store(a.ws_lse + it.slot + r, lse_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    // merged by the merge launch, which sees them after the kernel boundary
+    float* o = a.ws_o + size_t(it.slot + r) * D + d0;
+    for (int e = 0; e < n; ++e) o[e] = vals[e];
+    if (write_lse) a.ws_lse[it.slot + r] = lse_val;
   }
 }
 
-// Device-coherent read of a partial value (see the partial-row stores above).
+// Read of a partial value: device-coherent for in-launch groups (see the
+// partial-row stores above), a plain load in the merge launch.
+template <bool COHERENT>
 __device__ __forceinline__ float load_partial(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if constexpr (COHERENT) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else return *p;
 }
 
 // ----------------------------------------------------------------------------
@@ -682,9 +693,10 @@ constexpr int valu_lds_bytes() {
 // largest partial lse and the sum of the weights e^(lse_i - max) and writes
 // the final lse = max + ln(sum); then every thread takes independent (row,
 // 4-dim) units and sums the weighted, normalised partial rows.  Same formula
-// as the pages' merge step.  `red` is LDS for 2 * nrows floats.  Partial
-// values are read with device-coherent loads.
-template <int D>
+// as the pages' merge step.  `red` is LDS for 2 * nrows floats.  Inside the
+// attention launch (COHERENT) partial values are read with device-coherent
+// loads.
+template <int D, bool COHERENT>
 __device__ void merge_group(const AttnArgs& a, const MergeRec& g, float* red) {
   constexpr int CH = D / 4;
   const int tid = threadIdx.x;
@@ -698,10 +710,10 @@ __device__ void merge_group(const AttnArgs& a, const MergeRec& g, float* red) {
   for (int r = tid; r < g.nrows; r += kThreads) {
     const float* ls = a.ws_lse + g.slot0 + r;
     float mx = -INFINITY;
-    for (int i = 0; i < g.nsplit; ++i) mx = fmaxf(mx, load_partial(ls + size_t(i) * g.nrows));
+    for (int i = 0; i < g.nsplit; ++i) mx = fmaxf(mx, load_partial<COHERENT>(ls + size_t(i) * g.nrows));
     float wsum = 0.f;
     for (int i = 0; i < g.nsplit; ++i) {
-      const float li = load_partial(ls + size_t(i) * g.nrows);
+      const float li = load_partial<COHERENT>(ls + size_t(i) * g.nrows);
       wsum += (li == -INFINITY) ? 0.f : fast_exp2((li - mx) * kLog2e);
     }
     red[r] = mx;
@@ -716,11 +728,11 @@ __device__ void merge_group(const AttnArgs& a, const MergeRec& g, float* red) {
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     for (int i = 0; i < g.nsplit; ++i) {
       const size_t pr = size_t(g.slot0) + size_t(i) * g.nrows + r;
-      const float li = load_partial(a.ws_lse + pr);
+      const float li = load_partial<COHERENT>(a.ws_lse + pr);
       const float w = (li == -INFINITY) ? 0.f : fast_exp2((li - mx) * kLog2e) * inv;
       const float* o = a.ws_o + pr * D + 4 * c;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = fmaf(w, load_partial(o + e), acc[e]);
+      for (int e = 0; e < 4; ++e) acc[e] = fmaf(w, load_partial<COHERENT>(o + e), acc[e]);
     }
     store_result(a, sq, fin, D, r, 4 * c, acc, 4, false, 0.f);
   }
@@ -748,7 +760,7 @@ __device__ void finish_split(const AttnArgs& a, const ItemRec& it, int* last_fla
   }
   __syncthreads();
   if (!*last_flag) return;
-  merge_group<D>(a, a.groups[it.group], reinterpret_cast<float*>(last_flag) + 4);
+  merge_group<D, true>(a, a.groups[it.group], reinterpret_cast<float*>(last_flag) + 4);
   if (threadIdx.x == 0)
     __hip_atomic_store(a.counters + it.group, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -763,7 +775,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   if constexpr (MFMA) {
     if (it.waves > 0) {
       mfma_item<D, B>(a, it, reinterpret_cast<uint16_t*>(smem));
-      if (it.group >= 0) finish_split<D>(a, it, reinterpret_cast<int*>(smem));
+      if (it.group >= 0 && it.group < a.n_inlaunch) finish_split<D>(a, it, reinterpret_cast<int*>(smem));
       return;
     }
   }
@@ -771,7 +783,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
     valu_item<D, B, 1>(a, it, reinterpret_cast<float*>(smem));
   else
     valu_item<D, B, kValuMaxRows>(a, it, reinterpret_cast<float*>(smem));
-  if (it.group >= 0) finish_split<D>(a, it, reinterpret_cast<int*>(smem));
+  if (it.group >= 0 && it.group < a.n_inlaunch) finish_split<D>(a, it, reinterpret_cast<int*>(smem));
+}
+
+// Merge launch for split prefill tiles: one work-group per group, after the
+// attention launch (so plain loads see the partial rows).
+template <int D>
+__global__ __launch_bounds__(kThreads) void merge_kernel(AttnArgs a) {
+  __shared__ float red[2 * kMfmaTileRows];
+  merge_group<D, false>(a, a.groups[a.n_inlaunch + blockIdx.x], red);
 }
 
 // Append of one run (up to B consecutive new tokens of one sequence in one
@@ -1105,6 +1125,7 @@ extern "C" fg_status fg_attention_ragged(const fg_plan* plan, void* d_meta, cons
   a.hkv = plan->hkv;
   a.group = plan->group;
   a.n_mfma = plan->n_mfma;
+  a.n_inlaunch = plan->n_inlaunch_groups;
   a.scale_log2 = plan->scale * kLog2e;
   a.out_bf16 = out_dtype == FG_DTYPE_BF16;
 
@@ -1120,6 +1141,15 @@ extern "C" fg_status fg_attention_ragged(const fg_plan* plan, void* d_meta, cons
   } while (0)
     FG_SWITCH_DB(plan->head_dim, plan->block_size, FG_LAUNCH_ATTN);
 #undef FG_LAUNCH_ATTN
+    if (hipGetLastError() != hipSuccess) return FG_E_HIP;
+  }
+  const int32_t n_late = plan->n_merge_groups - plan->n_inlaunch_groups;
+  if (n_late > 0) {
+    ProfScope prof(FG_KERNEL_MERGE, s);
+    if (plan->head_dim == 64)
+      hipLaunchKernelGGL((merge_kernel<64>), dim3(unsigned(n_late)), dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((merge_kernel<128>), dim3(unsigned(n_late)), dim3(kThreads), 0, s, a);
     if (hipGetLastError() != hipSuccess) return FG_E_HIP;
   }
   return FG_OK;
@@ -1159,6 +1189,7 @@ extern "C" const char* fg_kernel_name(int32_t id) {
   switch (id) {
     case FG_KERNEL_APPEND: return "append_kernel";
     case FG_KERNEL_ATTENTION: return "attn_kernel";
+    case FG_KERNEL_MERGE: return "merge_kernel";
     default: return "unknown";
   }
 }

@@ -293,7 +293,7 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
     std::vector<Pending> mfma, valu;
     mfma.reserve(groups.size());
     valu.reserve(groups.size() * 2);
-    std::vector<MergeRec> merges;
+    std::vector<MergeRec> merges, late_merges;
     int64_t partial_rows = 0;
     int max_used = 1;
     int32_t order = 0;
@@ -315,12 +315,14 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
       k = ceil_div(grp.vis_end, chunk);
       max_used = std::max<int>(max_used, int(k));
       int32_t slot0 = -1;
+      // Split groups of at most one wavefront's rows merge inside the
+      // attention launch (group index >= 0 here); split tiles are merged by a
+      // merge launch (encoded -2 - index until the two lists are joined).
       int32_t group = -1;
       if (k > 1) {
         if (partial_rows + k * grp.nrows > INT32_MAX) return FG_E_RANGE;
         slot0 = int32_t(partial_rows);
         partial_rows += k * grp.nrows;
-        group = int32_t(merges.size());
         MergeRec m;
         m.seq = grp.seq;
         m.kv_head = grp.kv_head;
@@ -329,7 +331,13 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
         m.nsplit = int32_t(k);
         m.slot0 = slot0;
         m.pad0 = m.pad1 = 0;
-        merges.push_back(m);
+        if (grp.waves <= 1) {
+          group = int32_t(merges.size());
+          merges.push_back(m);
+        } else {
+          group = -2 - int32_t(late_merges.size());
+          late_merges.push_back(m);
+        }
       }
       for (int64_t i = 0; i < k; ++i) {
         Pending p;
@@ -348,6 +356,16 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
         (grp.waves ? mfma : valu).push_back(p);
       }
     }
+
+    // In-launch groups first, then the merge launch's; remap the items.
+    const int32_t n_inl = int32_t(merges.size());
+    auto remap = [n_inl](std::vector<Pending>& v) {
+      for (Pending& p : v)
+        if (p.item.group <= -2) p.item.group = n_inl + (-2 - p.item.group);
+    };
+    remap(mfma);
+    remap(valu);
+    merges.insert(merges.end(), late_merges.begin(), late_merges.end());
 
     // Longest first within each kind (ties keep plan order: deterministic).
     auto longest_first = [](const Pending& a, const Pending& b) {
@@ -373,6 +391,7 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
     plan->n_valu = int32_t(valu.size());
     plan->n_items = plan->n_mfma + plan->n_valu;
     plan->n_merge_groups = int32_t(merges.size());
+    plan->n_inlaunch_groups = n_inl;
     plan->n_partial_rows = int32_t(partial_rows);
     plan->max_splits_used = max_used;
     plan->target_cus = target_cus;
@@ -383,7 +402,7 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
     plan->off_runs = off;   off = align16(off + sizeof(RunRec) * runs.size());
     plan->off_items = off;  off = align16(off + sizeof(ItemRec) * size_t(plan->n_items));
     plan->off_merges = off; off = align16(off + sizeof(MergeRec) * merges.size());
-    plan->off_counters = off; off = align16(off + sizeof(int32_t) * merges.size());
+    plan->off_counters = off; off = align16(off + sizeof(int32_t) * size_t(n_inl));
     plan->blob.assign(std::max<size_t>(off, 16), 0);
     uint8_t* base = plan->blob.data();
     if (!seqs.empty()) memcpy(base + plan->off_seqs, seqs.data(), sizeof(SeqRec) * seqs.size());
@@ -432,6 +451,7 @@ extern "C" fg_status fg_plan_info(const fg_plan* p, fg_plan_info_t* o) {
   o->num_valu_items = p->n_valu;
   o->num_mfma_items = p->n_mfma;
   o->num_merge_groups = p->n_merge_groups;
+  o->num_inlaunch_merge_groups = p->n_inlaunch_groups;
   o->num_partial_rows = p->n_partial_rows;
   o->max_splits_used = p->max_splits_used;
   o->num_append_runs = p->n_runs;
@@ -459,6 +479,7 @@ extern "C" fg_status fg_plan_metadata(const fg_plan* p, void* host_dst, size_t b
     layout->num_runs = p->n_runs;
     layout->num_items = p->n_items;
     layout->num_merges = p->n_merge_groups;
+    layout->num_counters = p->n_inlaunch_groups;
   }
   return FG_OK;
 }

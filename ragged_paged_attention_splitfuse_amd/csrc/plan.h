@@ -27,6 +27,7 @@ struct fg_plan {
   int32_t n_mfma = 0;
   int32_t n_valu = 0;
   int32_t n_merge_groups = 0;   // row groups that were split (one MergeRec each)
+  int32_t n_inlaunch_groups = 0;  // the first of them, merged inside the attention launch
   int32_t n_partial_rows = 0;
   int32_t max_splits_used = 0;
   int32_t target_cus = 0;

@@ -46,8 +46,12 @@ def check_plan(plan, spec):
         assert (slot < 0) == (grp < 0) and -1 <= grp < len(merges)
         groups[(seq, kvh, row0, nrows)].append((kv0, kv1, slot, grp))
 
-    # one record and one zeroed counter per split group
-    assert len(meta["counters"]) == len(merges) and not meta["counters"].any()
+    # one record per split group; the in-launch groups (at most one wavefront's
+    # rows) come first and each has a zeroed counter, split tiles follow
+    n_inl = info["num_inlaunch_merge_groups"]
+    assert len(meta["counters"]) == n_inl and not meta["counters"].any()
+    for gi, m in enumerate(merges):
+        assert (int(m[3]) <= 32) == (gi < n_inl)
     merge_by_group = {}
     for gi, m in enumerate(merges):
         seq, kvh, row0, nrows, nsplit, slot0, pad0, pad1 = map(int, m)

@@ -153,10 +153,10 @@ def test_forced_splits_gqa_tiles():
 @pytest.mark.parametrize("name,splits", [("gqa8_d128_b64_mixed", 7), ("mha_d64_b32_mixed", 5),
                                          ("over64", 100)])
 def test_split_groups_merge_in_launch_and_rearm(name, splits):
-    # Split items merge inside the attention launch: the last split of a group
-    # to finish merges it and re-arms the group's counter.  Three launches on
-    # one upload must agree bit for bit, match the oracle, and leave every
-    # counter at zero.  "over64" has a decode split 71 ways (the merge reads
+    # Split decode groups merge inside the attention launch: the last split of
+    # a group to finish merges it and re-arms the group's counter (split tiles
+    # get a merge launch).  Three launches on one upload must agree bit for
+    # bit, match the oracle, and leave every counter at zero.  "over64" has a decode split 71 ways (the merge reads
     # split lse values 64 lanes at a time).
     if name == "over64":
         spec = wl.custom_spec("over64", [1, 1, 20], [9000, 300, 700], 8, 2, 128, 64, seed=27)
@@ -171,6 +171,9 @@ def test_split_groups_merge_in_launch_and_rearm(name, splits):
     assert plan.info["num_merge_groups"] > 0
     if name == "over64":
         assert plan.info["max_splits_used"] > 64
+    if name == "gqa8_d128_b64_mixed":
+        # both kinds: decode groups merged in the launch, split tiles after it
+        assert 0 < plan.info["num_inlaunch_merge_groups"] < plan.info["num_merge_groups"]
     meta = plan.upload()
     q, kn, vn = G.to_dev(tens.q), G.to_dev(tens.k_new), G.to_dev(tens.v_new)
     fgb.kv_append(plan, meta, kn, vn, kp, vp)
@@ -185,10 +188,10 @@ def test_split_groups_merge_in_launch_and_rearm(name, splits):
     for out, lse in runs[1:]:
         assert torch.equal(out, runs[0][0]) and torch.equal(lse, runs[0][1])
     raw = meta.cpu().numpy()[:plan.info["metadata_bytes"]].view(np.int32)
-    words = plan.info["num_merge_groups"]
+    words = plan.info["num_inlaunch_merge_groups"]
     start = plan_counter_offset(plan) // 4
     counters = raw[start:start + words]
-    assert words == plan.info["num_merge_groups"] and not counters.any()
+    assert len(counters) == words and not counters.any()
     o_ref, l_ref = G.oracle_pass(spec, tens)
     compare(runs[0][0], runs[0][1], o_ref, l_ref, f"in-launch merge {name}")
 
