@@ -161,7 +161,7 @@ fg_status fg_plan_pass(const fg_pass_desc* desc, fg_plan** out_plan);
 fg_status fg_plan_info(const fg_plan* plan, fg_plan_info_t* out);
 
 /* Copy the plan's metadata into d_meta (device, >= metadata_bytes,
- * caller-owned), asynchronously and in order on `stream`.  Plans up to 1 MiB
+ * caller-owned), asynchronously and in order on `stream`.  Plans up to 2 MiB
  * are staged through a library-owned ring of pinned host buffers (allocated on
  * first use, held until the process ends) and copied by a small kernel on the
  * same stream; larger ones use hipMemcpyAsync, in which case the plan must stay
@@ -181,7 +181,7 @@ fg_status fg_kv_append(const fg_plan* plan, const void* d_meta,
  * return d_meta holds the plan (once the stream gets there) and the pools hold
  * the pass's new K/V, bit-exact as fg_kv_append writes them.  The append reads
  * its run records from the pinned staging slot, so it does not wait for the
- * metadata copy.  Plans over 1 MiB, or a process where pinned staging could
+ * metadata copy.  Plans over 2 MiB, or a process where pinned staging could
  * not be allocated, fall back to the two separate steps. */
 fg_status fg_upload_append(const fg_plan* plan, void* d_meta, const void* k_new,
                            const void* v_new, void* k_pool, void* v_pool, void* stream);

@@ -943,7 +943,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // only after the event recorded behind its last upload has completed.
 // Plans larger than a slot fall back to hipMemcpyAsync.
 constexpr int kStageSlots = 8;
-constexpr size_t kStageSlotBytes = size_t(1) << 20;
+constexpr size_t kStageSlotBytes = size_t(2) << 20;
 
 struct StageSlot {
   void* host = nullptr;

@@ -57,12 +57,14 @@ struct ItemRec {
 
 // A split group: the rows of one item-row range whose KV range was cut into
 // `nsplit` items.  Split i of row r writes partial row slot0 + i * nrows + r.
-// Groups 0 .. n_inlaunch-1 (at most one wavefront's rows: decode rows, GQA
-// decode groups) are merged inside the attention launch by the work-group
+// Groups 0 .. n_inlaunch-1 (at most one wavefront's rows -- decode rows, GQA
+// decode groups -- split at most four ways) are merged inside the attention
+// launch by the work-group
 // that finishes the group's last split; each owns one int32 arrival counter
 // in the counter section (zero on upload, reset to zero by the merging
 // work-group).  The remaining groups (split prefill tiles, whose partials are
-// 64 KiB per split) are merged by a merge launch after the attention launch.
+// 64 KiB per split, and many-way splits) are merged by a merge launch after
+// the attention launch.
 struct MergeRec {
   int32_t seq;
   int32_t kv_head;

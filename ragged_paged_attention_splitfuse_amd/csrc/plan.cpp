@@ -60,6 +60,15 @@ constexpr double kFlopPerByte = 170.0;
 constexpr double kMfmaMinCost = 0.5;
 constexpr int kMfmaMinSplitTokens = 1024;
 constexpr int kMfmaSlotsPerCu = 2;
+// Split groups merged inside the attention launch: at most one wavefront's
+// rows, in plans of at most this many items per work-group slot.  Every split
+// item of such a group ends with a store drain and a device-scope atomic
+// round trip before it can exit, so a slot pays that latency once per item it
+// runs.  Measured: 64 decodes split 16 ways (55 items per slot) took 1,218 us
+// per pass in-launch and 1,064 us with a merge launch; the 70B-class decode
+// half (about one item per slot, 64 groups split 8 ways) took 59.0 us
+// in-launch and 64.5 us with the merge launch.
+constexpr int kInLaunchMaxItemsPerSlot = 4;
 
 size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -297,7 +306,12 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
     int64_t partial_rows = 0;
     int max_used = 1;
     int32_t order = 0;
-    for (const Group& grp : groups) {
+    // Split count and chunk of every group first: whether split groups may
+    // merge inside the attention launch depends on the plan's item count.
+    std::vector<int64_t> gk(groups.size()), gchunk(groups.size());
+    int64_t total_items = 0;
+    for (size_t gi = 0; gi < groups.size(); ++gi) {
+      const Group& grp = groups[gi];
       int64_t k;
       if (d->force_splits > 0) {
         k = d->force_splits;
@@ -312,12 +326,22 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
       }
       k = std::max<int64_t>(1, std::min<int64_t>(k, ceil_div(grp.vis_end, fg::kKvTile)));
       const int64_t chunk = ceil_div(ceil_div(grp.vis_end, k), fg::kKvTile) * fg::kKvTile;
-      k = ceil_div(grp.vis_end, chunk);
+      gk[gi] = ceil_div(grp.vis_end, chunk);
+      gchunk[gi] = chunk;
+      total_items += gk[gi];
+    }
+    const bool inlaunch_ok =
+        total_items <= int64_t(kInLaunchMaxItemsPerSlot) * target_cus * kMfmaSlotsPerCu;
+    for (size_t gi = 0; gi < groups.size(); ++gi) {
+      const Group& grp = groups[gi];
+      const int64_t k = gk[gi], chunk = gchunk[gi];
       max_used = std::max<int>(max_used, int(k));
       int32_t slot0 = -1;
       // Split groups of at most one wavefront's rows merge inside the
-      // attention launch (group index >= 0 here); split tiles are merged by a
-      // merge launch (encoded -2 - index until the two lists are joined).
+      // attention launch when the plan has few items per slot (group index
+      // >= 0 here); split tiles, and every group of a plan with many items per
+      // slot, are merged by a merge launch (encoded -2 - index until the two
+      // lists are joined).
       int32_t group = -1;
       if (k > 1) {
         if (partial_rows + k * grp.nrows > INT32_MAX) return FG_E_RANGE;
@@ -331,7 +355,7 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
         m.nsplit = int32_t(k);
         m.slot0 = slot0;
         m.pad0 = m.pad1 = 0;
-        if (grp.waves <= 1) {
+        if (grp.waves <= 1 && inlaunch_ok) {
           group = int32_t(merges.size());
           merges.push_back(m);
         } else {

@@ -47,11 +47,16 @@ def check_plan(plan, spec):
         groups[(seq, kvh, row0, nrows)].append((kv0, kv1, slot, grp))
 
     # one record per split group; the in-launch groups (at most one wavefront's
-    # rows) come first and each has a zeroed counter, split tiles follow
+    # rows, in plans with few items per slot) come first and each has a zeroed
+    # counter; split tiles follow, and so does every group of a plan with many
+    # items per slot
     n_inl = info["num_inlaunch_merge_groups"]
     assert len(meta["counters"]) == n_inl and not meta["counters"].any()
     for gi, m in enumerate(merges):
-        assert (int(m[3]) <= 32) == (gi < n_inl)
+        assert int(m[3]) <= 32 or gi >= n_inl
+    if n_inl:
+        assert n_inl == sum(1 for m in merges if int(m[3]) <= 32)
+        assert len(items) <= 4 * 2 * info["target_cus"]
     merge_by_group = {}
     for gi, m in enumerate(merges):
         seq, kvh, row0, nrows, nsplit, slot0, pad0, pad1 = map(int, m)
