@@ -241,6 +241,80 @@ def plan_counter_offset(plan):
     return int(lay.counters)
 
 
+def _bits_to_f32(bits):
+    """bf16 bit patterns (uint16) -> the same values as float32."""
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+ONE_HOT_CASES = {            # Hq, Hkv, D, B
+    "mha_d128_b64": (4, 4, 128, 64),
+    "gqa8_d128_b16": (16, 2, 128, 16),
+    "gqa4_d64_b32": (8, 2, 64, 32),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ONE_HOT_CASES))
+@pytest.mark.parametrize("splits", [0, 3])
+def test_one_hot_probe_block_boundaries(name, splits):
+    # Addressing pin without the oracle: every query is 40 * e_0 and the only
+    # nonzero key entry is K[t*][.][0] = 40 for a per-sequence target t* at or
+    # next to a block boundary, inside the cached context so every row sees
+    # it.  The target's score beats every other by >= 141, so each other weight
+    # is exp(-141), zero in fp32: O must be V[t*] bit for bit (fp32 output) and
+    # LSE the target score, for decodes and chunk tiles, split or not.
+    hq, hkv, d, b = ONE_HOT_CASES[name]
+    targets = [0, b - 1, b, 2 * b - 1, 2 * b, 3 * b + 5, 5 * b - 1, 5 * b]
+    ctx = [t + 1 + 37 * (i % 3) for i, t in enumerate(targets)]
+    q_lens = [1, 70, 1, 3, 40, 1, 130, 2]
+    spec = wl.custom_spec("probe", q_lens, ctx, hq, hkv, d, b, seed=51)
+    _log(f"[case] one-hot probe {name} splits={splits}")
+    base = wl.make_tensors(spec)
+    t_rows, h_rows = spec.num_tokens, int(spec.ctx_lens.sum())
+    q = np.zeros((t_rows, hq, d), np.float32)
+    q[:, :, 0] = 40.0
+    hk = np.zeros((h_rows, hkv, d), np.float32)
+    hcu = np.concatenate([[0], np.cumsum(spec.ctx_lens)])
+    for s, t in enumerate(targets):
+        hk[hcu[s] + t, :, 0] = 40.0
+    tens = wl.PassTensors(q=wl.bf16_round(q), k_new=wl.bf16_round(np.zeros((t_rows, hkv, d), np.float32)),
+                          v_new=base.v_new, hist_k=wl.bf16_round(hk), hist_v=base.hist_v)
+    _, _, _, out, lse, plan = G.full_gpu_pass(spec, tens=tens, force_splits=splits)
+    if splits:
+        assert plan.info["num_merge_groups"] > 0
+    out = out.cpu().numpy()
+    lse = lse.cpu().numpy().astype(np.float64)
+    g_ratio = hq // hkv
+    score = 1600.0 / np.sqrt(d)
+    row = 0
+    for s, t in enumerate(targets):
+        want = _bits_to_f32(base.hist_v[hcu[s] + t])          # [Hkv, D]
+        for _ in range(int(spec.q_lens[s])):
+            for h in range(hq):
+                assert np.array_equal(out[row, h], want[h // g_ratio]), (name, s, row, h)
+            row += 1
+    assert float(np.max(np.abs(lse - score))) <= 1e-4
+
+
+def test_sequence_order_permutes_rows_bit_identically():
+    # Shuffling the sequences of a pass permutes its output rows and changes
+    # nothing else: same split structure per sequence, same arithmetic.
+    spec = SMALL_SPECS["gqa8_d128_b64_mixed"]()
+    tens, _, _, out, lse, _ = G.full_gpu_pass(spec)
+    perm = np.array([3, 0, 4, 2, 1])
+    cu = np.concatenate([[0], np.cumsum(spec.q_lens)])
+    hcu = np.concatenate([[0], np.cumsum(spec.ctx_lens)])
+    rows = np.concatenate([np.arange(cu[s], cu[s + 1]) for s in perm])
+    hrows = np.concatenate([np.arange(hcu[s], hcu[s + 1]) for s in perm])
+    spec2 = wl.PassSpec(**{**spec.__dict__})
+    spec2.q_lens, spec2.ctx_lens = spec.q_lens[perm].copy(), spec.ctx_lens[perm].copy()
+    spec2.block_tables = spec.block_tables[perm].copy()
+    tens2 = wl.PassTensors(q=tens.q[rows], k_new=tens.k_new[rows], v_new=tens.v_new[rows],
+                           hist_k=tens.hist_k[hrows], hist_v=tens.hist_v[hrows])
+    _, _, _, out2, lse2, _ = G.full_gpu_pass(spec2, tens=tens2)
+    assert torch.equal(out2, out[torch.from_numpy(rows).to(out.device)])
+    assert torch.equal(lse2, lse[torch.from_numpy(rows).to(lse.device)])
+
+
 def test_block_permutation_is_bit_identical():
     spec = SMALL_SPECS["gqa8_d128_b64_mixed"]()
     tens, _, _, out, lse, _ = G.full_gpu_pass(spec)
