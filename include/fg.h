@@ -256,6 +256,18 @@ fg_status fg_profile_enable(int32_t on);
 fg_status fg_profile_read(double* total_ms, int32_t* launches, int32_t n_kernels);
 const char* fg_kernel_name(int32_t kernel_id);
 
+/* Achievable HBM read rate, for measurement only (no step of the method uses
+ * it): one launch on `stream` streams `bytes` (a multiple of 16) from the
+ * caller-owned device buffer buf (16-byte aligned) with 16-byte non-temporal
+ * loads, and writes one uint32 per thread into the caller-owned device buffer
+ * sink, which must hold at least 1024 bytes per compute unit of the current
+ * device (256 KiB on a 256-CU part; 1 MiB covers any).  Time it with events
+ * on the same stream.  FG_E_INVALID for null or misaligned pointers or a size
+ * not a multiple of 16, FG_E_WORKSPACE for a short sink, FG_E_HIP if the
+ * launch fails. */
+fg_status fg_probe_read_stream(const void* buf, size_t bytes, void* sink, size_t sink_bytes,
+                               void* stream);
+
 #ifdef __cplusplus
 }
 #endif

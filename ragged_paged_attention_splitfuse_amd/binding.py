@@ -87,6 +87,8 @@ SIGNATURES = {
     "fg_profile_enable": (ctypes.c_int32, [ctypes.c_int32]),
     "fg_profile_read": (ctypes.c_int32, [ctypes.POINTER(ctypes.c_double), _I32P, ctypes.c_int32]),
     "fg_kernel_name": (ctypes.c_char_p, [ctypes.c_int32]),
+    "fg_probe_read_stream": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                              ctypes.c_size_t, ctypes.c_void_p]),
 }
 
 
@@ -328,6 +330,14 @@ def fg_profile_read():
     cnt = (ctypes.c_int32 * n)()
     _check(lib().fg_profile_read(ms, cnt, n), "fg_profile_read")
     return {lib().fg_kernel_name(i).decode(): (ms[i], cnt[i]) for i in range(n)}
+
+
+def fg_probe_read_stream(buf, sink, stream=None):
+    """One read-stream launch over the whole uint8 device tensor `buf`
+    (measurement only); `sink` is a device tensor of >= 1024 bytes per CU."""
+    _check(lib().fg_probe_read_stream(_ptr(buf), int(buf.numel() * buf.element_size()), _ptr(sink),
+                                      int(sink.numel() * sink.element_size()), _stream(stream)),
+           "fg_probe_read_stream")
 
 
 # short aliases used by tests and bench

@@ -23,7 +23,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           f"-I{INCLUDE}", f"-I{HERE}"]
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
-SOURCES = [("fg_device.hip", True), ("plan.cpp", False)]
+SOURCES = [("fg_device.hip", True), ("fg_probe.hip", True), ("plan.cpp", False)]
 
 
 def hipcc():

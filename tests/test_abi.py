@@ -68,3 +68,12 @@ def test_struct_sizes_match_header_layout(tmp_path):
         assert int(got[name]) == ctypes.sizeof(cls), name
         for field, _ in cls._fields_:
             assert int(got[f"{name}.{field}"]) == getattr(cls, field).offset, (name, field)
+
+
+def test_read_stream_probe_rejects_bad_arguments_before_any_device_call():
+    lib = binding.lib()
+    assert lib.fg_probe_read_stream(None, 16, None, 1 << 20, None) == binding.FG_E_INVALID
+    # a size that is not a multiple of 16, or a misaligned buffer: rejected
+    # before the pointers are used
+    assert lib.fg_probe_read_stream(4096, 24, 8192, 1 << 20, None) == binding.FG_E_INVALID
+    assert lib.fg_probe_read_stream(4104, 32, 8192, 1 << 20, None) == binding.FG_E_INVALID
