@@ -79,6 +79,10 @@ struct AttnArgs {
 __device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
+// Non-temporal 16-byte load: the line is streamed rather than kept for reuse.
+__device__ __forceinline__ u32x4 ld16_nt(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
 __device__ __forceinline__ void st16(uint16_t* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -217,7 +221,12 @@ __device__ void valu_item(const AttnArgs& a, const ItemRec& it, float* smem) {
       kr[i] = u32x4{0u, 0u, 0u, 0u};
       if (tok < kv_valid) {
         const int blk = (B >= kValuSubTile) ? blk_u : bt[tok / B];
-        kr[i] = ld16(a.kpool + ((size_t(blk) * a.hkv + g) * B + tok % B) * D + 8 * kdc);
+        // A K load instruction reads whole 128-byte lines (TPI full rows) that
+        // no other load of this item touches again, so K streams past the
+        // caches.  V^T stays cached: at B = 64 a 32-token sub-tile reads half
+        // of each 128-byte row and the other half belongs to the next
+        // wavefront's sub-tile, which finds it in L2.
+        kr[i] = ld16_nt(a.kpool + ((size_t(blk) * a.hkv + g) * B + tok % B) * D + 8 * kdc);
       }
     }
     const int vt = t0 + 8 * vtc;

@@ -69,6 +69,15 @@ constexpr int kMfmaSlotsPerCu = 2;
 // half (about one item per slot, 64 groups split 8 ways) took 59.0 us
 // in-launch and 64.5 us with the merge launch.
 constexpr int kInLaunchMaxItemsPerSlot = 4;
+// Decode-only passes with several groups per slot (many sequences, lengths
+// spread widely): the longest groups are each about one slot's share, and the
+// launch ends with those few streams running alone.  Halving the split target
+// there splits only the longest ones.  Measured on MI355X, 64 decodes with
+// contexts log-uniform over 512..16000: attention + merge 682 -> 669 us at 1/2,
+// 673 us at 1/4; the 7B pass, its decode half and the 70B decode half are
+// untouched by the rule (tiles present, or about one group per slot).
+constexpr double kSkewedItemsPerSlot = 2.0;
+constexpr double kSkewedSplitFactor = 2.0;
 
 size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -287,7 +296,6 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
     }
 
     // ---- split each group's visible range [0, vis_end)
-    const double target = std::max(1.0, total_cost / (double(target_cus) * kItemsPerCu));
     int64_t tile_groups = 0;
     double tile_cost = 0.0;
     for (const Group& grp : groups)
@@ -295,6 +303,13 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
         ++tile_groups;
         tile_cost += grp.cost;
       }
+    // A pass of vector-ALU groups only, with at least kSkewedItemsPerSlot of
+    // them per work-group slot, halves the split target (see kSkewedSplitFactor).
+    const bool many_valu_groups =
+        tile_groups == 0 &&
+        double(groups.size()) >= kSkewedItemsPerSlot * double(target_cus) * kMfmaSlotsPerCu;
+    const double target = std::max(
+        1.0, total_cost / (double(target_cus) * kItemsPerCu * (many_valu_groups ? kSkewedSplitFactor : 1.0)));
     const double tile_target =
         tile_groups >= target_cus
             ? 1e300
