@@ -65,6 +65,37 @@ def test_long_decodes_are_split_short_ones_not():
     assert per_seq[1:].max() == 32     # one item per head, no split
 
 
+def test_tile_free_plan_fits_whole_rounds_of_slots():
+    """The 70B-class decode half (64 GQA groups) splits to at most one item per
+    work-group slot rather than spilling a few items into a second round, and
+    still covers every row once."""
+    spec = wl.config_spec("70b_decode32")
+    plan = plan_of(spec)
+    check_plan(plan, spec)
+    slots = CUS * 2
+    n = plan.info["num_items"]
+    assert slots * 3 // 4 < n <= slots
+    assert plan.info["max_splits_used"] > 1
+    # a plan with tiles is left alone: the 70B share keeps its decode splits
+    assert plan_of(wl.config_spec("70b_share4096")).info["num_items"] > slots
+
+
+def test_skewed_decode_only_pass_splits_only_its_longest_decodes():
+    """64 decodes with contexts spread over 512..16000: at two or more groups
+    per slot the split target halves, so the longest decodes split and the
+    short ones stay whole."""
+    spec = wl.config_spec("7b_decode64")
+    meta = check_plan(plan_of(spec), spec)
+    items = meta["items"]
+    per_seq = np.bincount(items[:, 0], minlength=spec.num_seqs) // spec.num_kv_heads
+    kv = np.asarray(spec.ctx_lens) + np.asarray(spec.q_lens)
+    assert per_seq[np.argmax(kv)] >= 2
+    assert (per_seq[kv <= np.median(kv)] == 1).all()
+    total = float(kv.sum()) * spec.num_kv_heads
+    half_target = total / (CUS * 2.0 * 2.0)
+    assert (per_seq[kv * 1.0 <= half_target] == 1).all()
+
+
 def _item_costs(items):
     lengths = (items[:, 5] - items[:, 4]).astype(np.float64)
     mf = items[:, 7] > 0
