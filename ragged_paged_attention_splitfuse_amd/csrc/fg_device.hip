@@ -929,14 +929,20 @@ struct ProfScope {
     if (!g_prof_on) return;
     std::lock_guard<std::mutex> lk(g_prof_mu);
     start = prof_event();
-    if (start) hipEventRecord(start, stream);
+    if (start && hipEventRecord(start, stream) != hipSuccess) {
+      g_prof_pool.push_back(start);  // not recorded: no measurement for this launch
+      start = nullptr;
+    }
   }
   ~ProfScope() {
     if (!start) return;
     std::lock_guard<std::mutex> lk(g_prof_mu);
     hipEvent_t stop = prof_event();
-    if (!stop) return;
-    hipEventRecord(stop, stream);
+    if (!stop || hipEventRecord(stop, stream) != hipSuccess) {
+      g_prof_pool.push_back(start);
+      if (stop) g_prof_pool.push_back(stop);
+      return;
+    }
     g_prof_recs.push_back({kind, start, stop});
   }
 };
