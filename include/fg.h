@@ -46,8 +46,10 @@
  *   q          [T, Hq, D]            bf16, tokens in sequence order
  *   k_new/v_new[T, Hkv, D]           bf16, same token order
  *   k_pool     [num_blocks, Hkv, B, D]  bf16  (slot-major within a block)
- *   v_pool     [num_blocks, Hkv, D, B]  bf16  (each block stored transposed:
- *                                      for every dim, B slots contiguous)
+ *   v_pool     [num_blocks, Hkv, B/S, D, S]  bf16, S = min(B, 32): each
+ *                                      block stored transposed in sub-blocks
+ *                                      of S slots (for every dim, S slots
+ *                                      contiguous); B <= 32 is one sub-block
  *   out        [T, Hq, D]            fp32 or bf16
  *   lse        [T, Hq]               fp32, natural log
  * where T = sum(q_lens), B = block_size, D = head_dim.  Token j of sequence s

@@ -37,8 +37,9 @@ Readings taken where the pages are silent (each is listed in the design notes):
 
 Cache layout (the contract the HIP path implements independently):
 * K pool: [num_blocks, num_kv_heads, block_size, head_dim]
-* V pool: [num_blocks, num_kv_heads, head_dim, block_size]
-  (each V block is stored transposed, token index fastest).
+* V pool: [num_blocks, num_kv_heads, block_size // S, head_dim, S] with
+  S = min(block_size, 32): each V block is stored transposed in sub-blocks of
+  S slots, token index fastest (one sub-block when block_size <= 32).
 """
 import math
 
@@ -90,8 +91,9 @@ def kv_append(k_pool, v_pool, q_lens, ctx_lens, block_tables, block_size, k_new,
         pos = int(ctx_lens[s]) + np.arange(n)
         blk = np.asarray(block_tables[s])[pos // block_size]
         off = pos % block_size
-        k_out[blk, :, off, :] = k_new[cu[s]:cu[s] + n]          # [n, Hkv, D]
-        v_out[blk, :, :, off] = v_new[cu[s]:cu[s] + n]          # [n, Hkv, D]
+        sub = v_pool.shape[4]
+        k_out[blk, :, off, :] = k_new[cu[s]:cu[s] + n]                      # [n, Hkv, D]
+        v_out[blk, :, off // sub, :, off % sub] = v_new[cu[s]:cu[s] + n]    # [n, Hkv, D]
     return k_out, v_out
 
 
@@ -105,7 +107,8 @@ def gather_sequence(k_pool, v_pool, table_row, length, block_size):
     ids = np.asarray(table_row[:nblk], dtype=np.int64)
     hkv, d = k_pool.shape[1], k_pool.shape[3]
     k = k_pool[ids].transpose(0, 2, 1, 3).reshape(nblk * block_size, hkv, d)[:length]
-    v = v_pool[ids].transpose(0, 3, 1, 2).reshape(nblk * block_size, hkv, d)[:length]
+    # [blocks, Hkv, sub-block, D, slot] -> [blocks, sub-block, slot, Hkv, D]
+    v = v_pool[ids].transpose(0, 2, 4, 1, 3).reshape(nblk * block_size, hkv, d)[:length]
     return k, v
 
 

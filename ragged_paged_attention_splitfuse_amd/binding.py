@@ -256,9 +256,11 @@ def _check_tensor(t, shape, dtype_name, what):
 
 
 def pool_shapes(num_blocks, num_kv_heads, block_size, head_dim):
-    """(K pool shape, V pool shape) of the layouts in include/fg.h."""
+    """(K pool shape, V pool shape) of the layouts in include/fg.h: V blocks
+    are stored transposed in sub-blocks of min(block_size, 32) slots."""
+    sub = min(block_size, 32)
     return ((num_blocks, num_kv_heads, block_size, head_dim),
-            (num_blocks, num_kv_heads, head_dim, block_size))
+            (num_blocks, num_kv_heads, block_size // sub, head_dim, sub))
 
 
 def fg_kv_append(plan, d_meta, k_new, v_new, k_pool, v_pool, stream=None):

@@ -4,8 +4,9 @@
 // Kernels
 //   append_kernel   one work-group per (append run, kv head): copies the new K
 //                   rows into their block (slot-major) and writes the new V
-//                   rows transposed into the block's [D][B] layout (8x8 tiles
-//                   transposed in registers, 16-byte stores).
+//                   rows transposed into the block's [B/S][D][S] layout,
+//                   S = min(B, 32) (8x8 tiles transposed in registers, 16-byte
+//                   stores).
 //   attn_kernel     one work-group per work item.  Items with many query rows
 //                   (prompt-chunk tiles, GQA groups) take the matrix-core path:
 //                   K/V stages of 64 tokens staged in LDS, S^T = K Q^T and
@@ -84,6 +85,16 @@ __device__ __forceinline__ u32x4 ld16_nt(const uint16_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 __device__ __forceinline__ void st16(uint16_t* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// Offset of (dim d, slot t) inside one (block, kv head) region of the V pool:
+// the block is stored transposed in sub-blocks of S = min(B, 32) slots, each
+// [D][S] with the slot index fastest.  Eight slots starting at a multiple of 8
+// are always 16 contiguous bytes.
+template <int D, int B>
+__device__ __forceinline__ int vt_off(int d, int t) {
+  constexpr int S = B < 32 ? B : 32;
+  return (t / S) * (D * S) + d * S + t % S;
+}
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -221,11 +232,9 @@ __device__ void valu_item(const AttnArgs& a, const ItemRec& it, float* smem) {
       kr[i] = u32x4{0u, 0u, 0u, 0u};
       if (tok < kv_valid) {
         const int blk = (B >= kValuSubTile) ? blk_u : bt[tok / B];
-        // A K load instruction reads whole 128-byte lines (TPI full rows) that
-        // no other load of this item touches again, so K streams past the
-        // caches.  V^T stays cached: at B = 64 a 32-token sub-tile reads half
-        // of each 128-byte row and the other half belongs to the next
-        // wavefront's sub-tile, which finds it in L2.
+        // Each K and V^T load instruction reads whole 128-byte lines (TPI full
+        // K rows; 16 dims of one V^T sub-block) that no other load of this
+        // item touches again, so both stream with the non-temporal hint.
         kr[i] = ld16_nt(a.kpool + ((size_t(blk) * a.hkv + g) * B + tok % B) * D + 8 * kdc);
       }
     }
@@ -235,7 +244,7 @@ __device__ void valu_item(const AttnArgs& a, const ItemRec& it, float* smem) {
       vr[i] = u32x4{0u, 0u, 0u, 0u};
       if (vt < kv_valid) {
         const int blk = (B >= kValuSubTile) ? blk_u : bt[vt / B];
-        vr[i] = ld16(a.vpool + ((size_t(blk) * a.hkv + g) * D + vd + 16 * i) * B + vt % B);
+        vr[i] = ld16_nt(a.vpool + (size_t(blk) * a.hkv + g) * D * B + vt_off<D, B>(vd + 16 * i, vt % B));
       }
     }
     if (vt < kv_valid && vt + 8 > kv_valid) {
@@ -464,7 +473,7 @@ __device__ void mfma_item(const AttnArgs& a, const ItemRec& it, uint16_t* lds) {
       vst[c] = u32x4{0u, 0u, 0u, 0u};
       if (full || p < kv_valid) {
         const int blk = bt[p / B];
-        vst[c] = ld16(a.vpool + ((size_t(blk) * a.hkv + kv_head_base) * D + d) * B + p % B);
+        vst[c] = ld16(a.vpool + (size_t(blk) * a.hkv + kv_head_base) * D * B + vt_off<D, B>(d, p % B));
         if (!full && p + 8 > kv_valid) vst[c] = zero_tail(vst[c], p, kv_valid);
       }
     }
@@ -521,7 +530,7 @@ __device__ void mfma_item(const AttnArgs& a, const ItemRec& it, uint16_t* lds) {
 #pragma unroll
     for (int i = 0; i < VSEG_W; ++i) {
       const int u = 64 * (i * kWaves + wave) + lane;
-      voff[i] = (u / VU) * B + 8 * min(u % VU, kKvTile / 8 - 1);
+      voff[i] = vt_off<D, B>(u / VU, 8 * min(u % VU, kKvTile / 8 - 1));
     }
   }
   auto dma_stage = [&](int tb, int buf) {
@@ -856,7 +865,7 @@ __device__ __forceinline__ void append_run(const RunRec run, const int g, const 
       }
     if (full) {
 #pragma unroll
-      for (int d = 0; d < 8; ++d) st16(vblk + size_t(8 * dg + d) * B + s0, out[d]);
+      for (int d = 0; d < 8; ++d) st16(vblk + vt_off<D, B>(8 * dg + d, s0), out[d]);
     } else {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -865,7 +874,7 @@ __device__ __forceinline__ void append_run(const RunRec run, const int g, const 
 #pragma unroll
         for (int d = 0; d < 8; ++d) {
           const uint32_t w = out[d][u >> 1];
-          vblk[size_t(8 * dg + d) * B + s0 + u] = uint16_t((u & 1) ? (w >> 16) : (w & 0xffffu));
+          vblk[vt_off<D, B>(8 * dg + d, s0 + u)] = uint16_t((u & 1) ? (w >> 16) : (w & 0xffffu));
         }
       }
     }

@@ -266,12 +266,14 @@ def make_tensors(spec):
 def empty_pool_bits(spec, poison=False):
     """Fresh K and V pools filled with 0 or with bf16 NaN (poison mode).
 
-    Only the element counts matter here; both pools hold
-    num_blocks * num_kv_heads * block_size * head_dim elements.
+    Both pools hold num_blocks * num_kv_heads * block_size * head_dim
+    elements; the V pool's blocks are transposed sub-blocks of
+    min(block_size, 32) slots, [num_blocks, Hkv, block_size / S, D, S].
     """
     fill = BF16_NAN if poison else 0
+    sub = min(spec.block_size, 32)
     shape = (spec.num_blocks, spec.num_kv_heads, spec.block_size, spec.head_dim)
-    tshape = (spec.num_blocks, spec.num_kv_heads, spec.head_dim, spec.block_size)
+    tshape = (spec.num_blocks, spec.num_kv_heads, spec.block_size // sub, spec.head_dim, sub)
     return np.full(shape, fill, np.uint16), np.full(tshape, fill, np.uint16)
 
 

@@ -373,8 +373,9 @@ def test_chunked_prompt_matches_single_pass():
 def test_empty_pass_launches_nothing():
     plan = fgb.Plan([], [], np.zeros((0, 1), np.int32), 4, 4, 64, 16, 8, target_cus=0)
     meta = plan.upload()
-    kp = torch.zeros((8, 4, 16, 64), dtype=torch.bfloat16, device="cuda")
-    vp = torch.zeros((8, 4, 64, 16), dtype=torch.bfloat16, device="cuda")
+    kshape, vshape = fgb.pool_shapes(8, 4, 16, 64)
+    kp = torch.zeros(kshape, dtype=torch.bfloat16, device="cuda")
+    vp = torch.zeros(vshape, dtype=torch.bfloat16, device="cuda")
     e = torch.empty((0, 4, 64), dtype=torch.bfloat16, device="cuda")
     fgb.kv_append(plan, meta, e, e, kp, vp)
     fgb.attention_ragged(plan, meta, e, kp, vp, torch.empty((0, 4, 64), device="cuda"))

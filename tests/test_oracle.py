@@ -51,14 +51,18 @@ def _tiny_spec(q_lens, ctx_lens, hq=4, hkv=4, d=16, b=4, seed=11, nb=None):
     return wl.custom_spec("t", q_lens, ctx_lens, hq, hkv, d, b, seed, num_blocks=nb)
 
 
-def test_append_places_every_element_by_its_flat_address():
-    spec = _tiny_spec([5, 1, 9], [3, 6, 0], hkv=2, hq=2, d=8, b=4, nb=40)
-    t, hkv, d, b = spec.num_tokens, 2, 8, 4
+@pytest.mark.parametrize("b", [4, 64])
+def test_append_places_every_element_by_its_flat_address(b):
+    # V blocks are transposed sub-blocks of S = min(b, 32) slots: b = 4 is one
+    # sub-block, b = 64 two, and the chunk of 70 tokens crosses both.
+    spec = _tiny_spec([5, 1, 70], [3, 6, 0], hkv=2, hq=2, d=8, b=b, nb=40)
+    t, hkv, d = spec.num_tokens, 2, 8
+    sub = min(b, 32)
     ids = np.arange(1, t * hkv * d + 1, dtype=np.uint16).reshape(t, hkv, d)
     vids = (ids + 20000).astype(np.uint16)
     canary = 0x1234
     kp = np.full((spec.num_blocks, hkv, b, d), canary, np.uint16)
-    vp = np.full((spec.num_blocks, hkv, d, b), canary, np.uint16)
+    vp = np.full((spec.num_blocks, hkv, b // sub, d, sub), canary, np.uint16)
     ko, vo = ora.kv_append(kp, vp, spec.q_lens, spec.ctx_lens, spec.block_tables, b, ids, vids)
     kf, vf = ko.reshape(-1), vo.reshape(-1)
     touched = np.zeros(kf.size, bool)
@@ -71,7 +75,7 @@ def test_append_places_every_element_by_its_flat_address():
             for g in range(hkv):
                 for e in range(d):
                     kaddr = ((blk * hkv + g) * b + off) * d + e
-                    vaddr = ((blk * hkv + g) * d + e) * b + off
+                    vaddr = (blk * hkv + g) * d * b + (off // sub) * (d * sub) + e * sub + off % sub
                     assert kf[kaddr] == ids[row, g, e]
                     assert vf[vaddr] == vids[row, g, e]
                     touched[kaddr] = True
@@ -338,7 +342,7 @@ def test_chunked_prompt_equals_single_chunk():
     v = _bits(rng.standard_normal((p, hkv, d)))
     table = np.array([[5, 0, 3, 7, 1, 6]], np.int32)
     kp0 = np.zeros((8, hkv, b, d), np.uint16)
-    vp0 = np.zeros((8, hkv, d, b), np.uint16)
+    vp0 = np.zeros((8, hkv, 1, d, b), np.uint16)     # b = 8: one V sub-block per block
     kp, vp = ora.kv_append(kp0, vp0, [p], [0], table, b, k, v)
     o_one, l_one = ora.attend(q, kp, vp, [p], [0], table, b, hkv)
     kp, vp = kp0, vp0
