@@ -67,7 +67,9 @@
 extern "C" {
 #endif
 
-#define FG_ABI_VERSION 3
+/* 3: d_meta of fg_attention_ragged is writable (split-group counters).
+ * 4: V pool blocks stored in transposed sub-blocks of min(B, 32) slots. */
+#define FG_ABI_VERSION 4
 
 typedef int32_t fg_status;
 

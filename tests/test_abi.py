@@ -35,7 +35,7 @@ def test_binding_covers_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert binding.fg_abi_version() == 3
+    assert binding.fg_abi_version() == 4
     assert binding.status_string(0) == "ok"
     assert "twice" in binding.status_string(binding.FG_E_ALIAS)
     assert binding.status_string(12345) == "unknown status"
