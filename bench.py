@@ -384,7 +384,8 @@ def knobs_of(args, fgb):
     return {"target_cus": args.target_cus, "split_policy": policy, "force_splits": args.force_splits}
 
 
-def measure_pass(torch, fgb, spec, tens, dev, stream, knobs, steps, warmup, separate=False):
+def measure_pass(torch, fgb, spec, tens, dev, stream, knobs, steps, warmup, separate=False,
+                 events="timed-attention"):
     """Set up pools and inputs of one pass, then time `steps` passes (plan,
     upload + append in one launch, attention; `separate` uses the two-launch
     upload and append) back to back after `warmup` untimed ones.
@@ -415,7 +416,7 @@ def measure_pass(torch, fgb, spec, tens, dev, stream, knobs, steps, warmup, sepa
 
     host_plan_s = []
 
-    def step(keep):
+    def step(keep, attention=True):
         h0 = time.perf_counter()
         plan = fgb.Plan.from_spec(spec, **knobs)
         host_plan_s.append(time.perf_counter() - h0)
@@ -424,7 +425,8 @@ def measure_pass(torch, fgb, spec, tens, dev, stream, knobs, steps, warmup, sepa
             fgb.kv_append(plan, meta, kn, vn, kp, vp, stream)
         else:
             fgb.upload_append(plan, meta, kn, vn, kp, vp, stream)
-        fgb.attention_ragged(plan, meta, q, kp, vp, out, lse, workspace=ws, stream=stream)
+        if attention:
+            fgb.attention_ragged(plan, meta, q, kp, vp, out, lse, workspace=ws, stream=stream)
         keep.append(plan)
 
     keep = []
@@ -434,26 +436,40 @@ def measure_pass(torch, fgb, spec, tens, dev, stream, knobs, steps, warmup, sepa
     keep.clear()
     host_plan_s.clear()
 
-    # The timed passes run without the library's per-launch events; a second
-    # loop of the same passes with the events on gives the per-kernel times.
-    fgb.fg_profile_enable(False)
+    # Per-kernel times come from the library's HIP events on the launch stream.
+    # events="timed-attention": the timed passes bracket the attention (and
+    # merge) launches, the kernels `roofline` reports, and a second loop of the
+    # same passes' upload+append launches alone times that launch.  "timed": the timed passes
+    # bracket every launch.  "separate": the timed passes run without events
+    # and a second loop brackets every launch.
+    in_loop = {"timed": None, "timed-attention": (fgb.FG_KERNEL_ATTENTION, fgb.FG_KERNEL_MERGE),
+               "separate": ()}[events]
+    fgb.fg_profile_read()
+    if in_loop != ():
+        fgb.fg_profile_enable(True, in_loop)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
         step(keep)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    keep.clear()
-    plan_s_timed = list(host_plan_s)
-    fgb.fg_profile_read()
-    fgb.fg_profile_enable(True)
-    for _ in range(steps):
-        step(keep)
-    torch.cuda.synchronize()
     fgb.fg_profile_enable(False)
     kern = fgb.fg_profile_read()
     keep.clear()
-    host_plan_s[:] = plan_s_timed
+    if events != "timed":
+        plan_s_timed = list(host_plan_s)
+        append_only = events == "timed-attention"
+        fgb.fg_profile_enable(True, (fgb.FG_KERNEL_APPEND,) if append_only else None)
+        for _ in range(steps):
+            step(keep, attention=not append_only)
+        torch.cuda.synchronize()
+        fgb.fg_profile_enable(False)
+        more = fgb.fg_profile_read()
+        keep.clear()
+        host_plan_s[:] = plan_s_timed
+        for name, (ms, n) in more.items():
+            if n and not kern[name][1]:
+                kern[name] = (ms, n)
     return {"step": step, "keep": keep, "kern": kern, "info": info, "host_plan_s": host_plan_s,
             "ms_per_step": (t1 - t0) * 1e3 / steps}
 
@@ -478,7 +494,7 @@ def run_sweep(args, torch, fgb, wl, dev, stream, knobs):
         tens = wl.make_tensors(spec)
         alg = algorithmic(spec)
         m = measure_pass(torch, fgb, spec, tens, dev, stream, knobs, args.steps, args.warmup,
-                         args.separate_append)
+                         args.separate_append, args.kernel_events)
         ku = kernel_us(m["kern"])
         pass_us = m["ms_per_step"] * 1e3
         rows.append({"budget": budget, "pass_us": round(pass_us, 2),
@@ -531,6 +547,11 @@ def main():
                     help="planner split-count policy (speed only; results are identical)")
     ap.add_argument("--force-splits", type=int, default=0,
                     help="static split count for every row group (FlashDecoding-style)")
+    ap.add_argument("--kernel-events", choices=["timed-attention", "timed", "separate"],
+                    default="timed-attention",
+                    help="where the per-launch HIP events go: around the attention launches "
+                         "of the timed passes (default; upload+append timed in a second loop), "
+                         "around every launch of the timed passes, or only in a second loop")
     ap.add_argument("--separate-append", action="store_true",
                     help="upload the plan and append K/V in two launches instead of one")
     ap.add_argument("--serve-policy", choices=["splitfuse", "orca", "prefill_first"],
@@ -578,7 +599,7 @@ def main():
     t, hq, d = spec.num_tokens, spec.num_q_heads, spec.head_dim
     knobs = knobs_of(args, fgb)
     m = measure_pass(torch, fgb, spec, tens, dev, stream, knobs, args.steps, args.warmup,
-                     args.separate_append)
+                     args.separate_append, args.kernel_events)
     step, keep, kern, info = m["step"], m["keep"], m["kern"], m["info"]
     host_plan_s, ms_per_step = m["host_plan_s"], m["ms_per_step"]
 

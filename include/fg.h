@@ -244,11 +244,12 @@ fg_status fg_plan_metadata(const fg_plan* plan, void* host_dst, size_t bytes,
                            fg_plan_layout_t* layout);
 
 /* ---- measurement hooks ------------------------------------------------------
- * When enabled, the library brackets each of its kernel launches with HIP
- * events recorded on the launch stream.  fg_profile_read waits for the
- * recorded events, writes per-kernel totals (milliseconds and launch counts,
- * indexed by the FG_KERNEL_* ids) and clears the record.  Off by default; the
- * record is process-wide and not thread-safe. */
+ * fg_profile_enable(mask): bit (1 << FG_KERNEL_x) of mask makes the library
+ * bracket each launch of that kernel with HIP events recorded on the launch
+ * stream; 0 turns it off, -1 brackets every kernel.  fg_profile_read waits for
+ * the recorded events, writes per-kernel totals (milliseconds and launch
+ * counts, indexed by the FG_KERNEL_* ids) and clears the record.  Off by
+ * default; the record is process-wide and not thread-safe. */
 enum {
   FG_KERNEL_APPEND = 0,
   FG_KERNEL_ATTENTION = 1,

@@ -321,8 +321,13 @@ def fg_attention_ragged(plan, d_meta, q, k_pool, v_pool, out, lse=None, workspac
     return workspace
 
 
-def fg_profile_enable(on=True):
-    _check(lib().fg_profile_enable(1 if on else 0), "fg_profile_enable")
+def fg_profile_enable(on=True, kernels=None):
+    """Bracket launches with HIP events: every kernel, or only the FG_KERNEL_*
+    ids in `kernels`; on=False turns it off."""
+    mask = 0
+    if on:
+        mask = -1 if kernels is None else sum(1 << int(k) for k in kernels)
+    _check(lib().fg_profile_enable(int(mask)), "fg_profile_enable")
 
 
 def fg_profile_read():

@@ -915,7 +915,7 @@ struct ProfRec {
   hipEvent_t start, stop;
 };
 std::mutex g_prof_mu;
-bool g_prof_on = false;
+uint32_t g_prof_mask = 0;  // bit k: bracket launches of FG_KERNEL k
 std::vector<ProfRec> g_prof_recs;
 std::vector<hipEvent_t> g_prof_pool;
 
@@ -935,7 +935,7 @@ struct ProfScope {
   hipStream_t stream;
   hipEvent_t start = nullptr;
   ProfScope(int k, hipStream_t s) : kind(k), stream(s) {
-    if (!g_prof_on) return;
+    if (((g_prof_mask >> kind) & 1u) == 0) return;
     std::lock_guard<std::mutex> lk(g_prof_mu);
     start = prof_event();
     if (start && hipEventRecord(start, stream) != hipSuccess) {
@@ -1179,9 +1179,9 @@ extern "C" fg_status fg_attention_ragged(const fg_plan* plan, void* d_meta, cons
   return FG_OK;
 }
 
-extern "C" fg_status fg_profile_enable(int32_t on) {
+extern "C" fg_status fg_profile_enable(int32_t mask) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  g_prof_on = on != 0;
+  g_prof_mask = static_cast<uint32_t>(mask);
   return FG_OK;
 }
 
