@@ -420,7 +420,9 @@ __device__ void mfma_item(const AttnArgs& a, const ItemRec& it, uint16_t* lds) {
   constexpr int KCH = kKvTile * CPR / kThreads;       // K chunks per thread per stage
   constexpr int VCH = D * (kKvTile / 8) / kThreads;   // V^T chunks per thread per stage
   static_assert(KCH * kThreads == kKvTile * CPR && VCH * kThreads == D * kKvTile / 8, "stage split");
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // The wavefront index is uniform; reading it as a scalar keeps the staging
+  // segments' LDS addresses in scalar registers.
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
   const SeqRec sq = a.seqs[it.seq];
   const int32_t* bt = a.bt + sq.bt_off;
