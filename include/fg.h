@@ -156,8 +156,16 @@ typedef struct fg_plan_info_t {
 } fg_plan_info_t;
 
 /* Build the plan of one pass (host only, no device call unless
- * desc->target_cus == 0).  Validates every input (see fg_status).  On success
- * *out_plan receives a plan owned by the library; free it with
+ * desc->target_cus == 0): the split-KV work list whose split counts follow
+ * each request's length and the compute-unit count ("DeepSpeed-FastGen Guide:
+ * Dynamic SplitKV Serving", section "1. Dynamic SplitKV Attention", and its
+ * "Step 2: Dynamic SplitKV Allocation Engine").  Validates every input: null
+ * pointers, bad counts or knobs -> FG_E_INVALID; block ids out of range or a
+ * short table row -> FG_E_RANGE; a block used twice -> FG_E_ALIAS; head_dim or
+ * block_size not supported -> FG_E_UNSUPPORTED; host allocation failure ->
+ * FG_E_NOMEM; a failed device query for target_cus == 0 -> FG_E_HIP.  The
+ * desc's arrays are copied, so the caller may free them on return.  On
+ * success *out_plan receives a plan owned by the library; free it with
  * fg_plan_destroy.  Deterministic: the same desc gives a byte-identical plan. */
 fg_status fg_plan_pass(const fg_pass_desc* desc, fg_plan** out_plan);
 
@@ -165,17 +173,25 @@ fg_status fg_plan_pass(const fg_pass_desc* desc, fg_plan** out_plan);
 fg_status fg_plan_info(const fg_plan* plan, fg_plan_info_t* out);
 
 /* Copy the plan's metadata into d_meta (device, >= metadata_bytes,
- * caller-owned), asynchronously and in order on `stream`.  Plans up to 2 MiB
+ * caller-owned, 16-byte aligned), asynchronously and in order on `stream`.
+ * FG_E_INVALID for a null plan or a null or misaligned d_meta, FG_E_HIP if a
+ * copy or launch fails.  Plans up to 2 MiB
  * are staged through a library-owned ring of pinned host buffers (allocated on
  * first use, held until the process ends) and copied by a small kernel on the
  * same stream; larger ones use hipMemcpyAsync, in which case the plan must stay
  * alive until the stream has passed the copy. */
 fg_status fg_plan_upload(const fg_plan* plan, void* d_meta, void* stream);
 
-/* Scatter the pass's new K and V into their cache slots (asynchronous).
- * k_new, v_new: [T, Hkv, D] bf16; k_pool, v_pool: pools in the layouts above.
- * Writes exactly T*Hkv K rows and T*Hkv V columns; no other byte of the pools
- * changes.  Bit-exact copy. */
+/* Scatter the pass's new K and V into their cache slots (asynchronous): token
+ * j of sequence s goes to block block_tables[s][p / B], slot p % B, with
+ * p = ctx_lens[s] + j ("DeepSpeed-FastGen Guide: Dynamic SplitKV Serving",
+ * section "3. Paged KV Memory Management with Zero Overhead").  d_meta must
+ * hold this plan's uploaded metadata (read only here).  k_new, v_new:
+ * [T, Hkv, D] bf16; k_pool, v_pool: pools in the layouts above; all
+ * caller-owned.  Writes exactly T*Hkv K rows and T*Hkv V columns; no other
+ * byte of the pools changes.  Bit-exact copy.  FG_E_INVALID for a null or
+ * misaligned pointer (a pass with nothing to append returns FG_OK at once),
+ * FG_E_HIP if the launch fails. */
 fg_status fg_kv_append(const fg_plan* plan, const void* d_meta,
                        const void* k_new, const void* v_new,
                        void* k_pool, void* v_pool, void* stream);
@@ -193,7 +209,13 @@ fg_status fg_upload_append(const fg_plan* plan, void* d_meta, const void* k_new,
 /* Attention of every query row of the pass over its sequence's cached keys
  * 0 .. ctx + j (inclusive causal bound), read through the block tables
  * (asynchronous; one kernel launch, plus a merge launch when the plan splits
- * prefill tiles).  The pools must already hold this pass's
+ * prefill tiles).  Split KV ranges are computed as partial softmax results and
+ * merged by log-sum-exp ("DeepSpeed-FastGen Guide: Dynamic SplitKV Serving",
+ * section "1. Dynamic SplitKV Attention", two-phase softmax; merge weights are
+ * the partials' log-sum-exp values).  Errors: FG_E_UNSUPPORTED for an unknown
+ * out_dtype, FG_E_INVALID for a null or misaligned pointer, FG_E_WORKSPACE for
+ * a missing, short or misaligned workspace, FG_E_HIP if a launch fails; a plan
+ * with no rows returns FG_OK without a launch.  The pools must already hold this pass's
  * K/V (append first, on the same stream).  q: [T, Hq, D] bf16.  out: [T, Hq, D]
  * of out_dtype (FG_DTYPE_F32 or FG_DTYPE_BF16).  lse: [T, Hq] fp32 or NULL.
  * d_ws: caller-owned workspace of >= workspace_bytes (may be NULL when that is
