@@ -77,3 +77,14 @@ def test_read_stream_probe_rejects_bad_arguments_before_any_device_call():
     # before the pointers are used
     assert lib.fg_probe_read_stream(4096, 24, 8192, 1 << 20, None) == binding.FG_E_INVALID
     assert lib.fg_probe_read_stream(4104, 32, 8192, 1 << 20, None) == binding.FG_E_INVALID
+
+
+def test_profile_mask_toggles_without_a_device():
+    # Enabling, selecting kernels and reading an empty record make no device call.
+    binding.fg_profile_enable(True, (binding.FG_KERNEL_ATTENTION,))
+    assert binding.fg_profile_read() == {"append_kernel": (0.0, 0), "attn_kernel": (0.0, 0),
+                                         "merge_kernel": (0.0, 0)}
+    binding.fg_profile_enable(True)
+    binding.fg_profile_enable(False)
+    lib = binding.lib()
+    assert lib.fg_profile_read(None, None, -1) == binding.FG_E_INVALID
