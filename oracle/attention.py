@@ -74,6 +74,15 @@ def _cu(q_lens):
     return cu
 
 
+def _v_sub(v_pool, block_size):
+    """Slots per transposed V sub-block, min(block_size, 32), checked against
+    the pool's shape [num_blocks, Hkv, block_size // S, D, S]."""
+    sub = min(int(block_size), 32)
+    if v_pool.ndim != 5 or v_pool.shape[2] * v_pool.shape[4] != block_size or v_pool.shape[4] != sub:
+        raise ValueError(f"V pool shape {v_pool.shape} is not [blocks, Hkv, {block_size // sub}, D, {sub}]")
+    return sub
+
+
 def kv_append(k_pool, v_pool, q_lens, ctx_lens, block_tables, block_size, k_new, v_new):
     """Write each new token's K and V into its cache slot; return new pools.
 
@@ -83,6 +92,7 @@ def kv_append(k_pool, v_pool, q_lens, ctx_lens, block_tables, block_size, k_new,
     is value-preserving for any dtype (bf16 bits in, bf16 bits out).
     (FastGen Guide, section "3. Paged KV Memory Management with Zero Overhead".)
     """
+    sub = _v_sub(v_pool, block_size)
     k_out = np.array(k_pool, copy=True)
     v_out = np.array(v_pool, copy=True)
     cu = _cu(q_lens)
@@ -91,7 +101,6 @@ def kv_append(k_pool, v_pool, q_lens, ctx_lens, block_tables, block_size, k_new,
         pos = int(ctx_lens[s]) + np.arange(n)
         blk = np.asarray(block_tables[s])[pos // block_size]
         off = pos % block_size
-        sub = v_pool.shape[4]
         k_out[blk, :, off, :] = k_new[cu[s]:cu[s] + n]                      # [n, Hkv, D]
         v_out[blk, :, off // sub, :, off % sub] = v_new[cu[s]:cu[s] + n]    # [n, Hkv, D]
     return k_out, v_out
@@ -106,6 +115,7 @@ def gather_sequence(k_pool, v_pool, table_row, length, block_size):
     nblk = -(-int(length) // block_size)
     ids = np.asarray(table_row[:nblk], dtype=np.int64)
     hkv, d = k_pool.shape[1], k_pool.shape[3]
+    _v_sub(v_pool, block_size)
     k = k_pool[ids].transpose(0, 2, 1, 3).reshape(nblk * block_size, hkv, d)[:length]
     # [blocks, Hkv, sub-block, D, slot] -> [blocks, sub-block, slot, Hkv, D]
     v = v_pool[ids].transpose(0, 2, 4, 1, 3).reshape(nblk * block_size, hkv, d)[:length]
