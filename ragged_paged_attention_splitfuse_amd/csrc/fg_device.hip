@@ -742,19 +742,49 @@ __device__ void merge_group(const AttnArgs& a, const MergeRec& g, float* red) {
                  wsum > 0.f ? mx + fast_log2(wsum) * kLn2 : -INFINITY);
   }
   __syncthreads();
-  for (int u = tid; u < g.nrows * CH; u += kThreads) {
-    const int r = u / CH, c = u % CH;
-    const float mx = red[r], inv = red[g.nrows + r];
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int i = 0; i < g.nsplit; ++i) {
-      const size_t pr = size_t(g.slot0) + size_t(i) * g.nrows + r;
-      const float li = load_partial<COHERENT>(a.ws_lse + pr);
-      const float w = (li == -INFINITY) ? 0.f : fast_exp2((li - mx) * kLog2e) * inv;
-      const float* o = a.ws_o + pr * D + 4 * c;
+  // Four (row, 4-dim) units per thread per pass, their loads issued together.
+  constexpr int UPT = 4;
+  const int units = g.nrows * CH;
+  for (int u0 = tid; u0 < units; u0 += UPT * kThreads) {
+    float acc[UPT][4];
+    int rr[UPT], cc[UPT];
+    bool ok[UPT];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = fmaf(w, load_partial<COHERENT>(o + e), acc[e]);
+    for (int j = 0; j < UPT; ++j) {
+      const int u = u0 + j * kThreads;
+      ok[j] = u < units;
+      rr[j] = ok[j] ? u / CH : 0;
+      cc[j] = ok[j] ? u % CH : 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[j][e] = 0.f;
     }
-    store_result(a, sq, fin, D, r, 4 * c, acc, 4, false, 0.f);
+    for (int i = 0; i < g.nsplit; ++i) {
+      float li[UPT], ov[UPT][4];
+#pragma unroll
+      for (int j = 0; j < UPT; ++j) {
+        const size_t pr = size_t(g.slot0) + size_t(i) * g.nrows + rr[j];
+        li[j] = ok[j] ? load_partial<COHERENT>(a.ws_lse + pr) : -INFINITY;
+        const float* o = a.ws_o + pr * D + 4 * cc[j];
+        if constexpr (COHERENT) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ov[j][e] = ok[j] ? load_partial<true>(o + e) : 0.f;
+        } else {
+          const f32x4 v = ok[j] ? *reinterpret_cast<const f32x4*>(o) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ov[j][e] = v[e];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < UPT; ++j) {
+        const float mx = red[rr[j]], inv = red[g.nrows + rr[j]];
+        const float w = (li[j] == -INFINITY) ? 0.f : fast_exp2((li[j] - mx) * kLog2e) * inv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[j][e] = fmaf(w, ov[j][e], acc[j][e]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < UPT; ++j)
+      if (ok[j]) store_result(a, sq, fin, D, rr[j], 4 * cc[j], acc[j], 4, false, 0.f);
   }
 }
 
