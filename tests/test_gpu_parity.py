@@ -73,6 +73,19 @@ def test_attention_matches_oracle_small(name):
     compare(out, lse, o_ref, l_ref, name)
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_random_compositions_match_oracle(seed):
+    from tests._random_passes import random_pass
+    spec, knobs = random_pass(seed)
+    _log(f"[case] random {seed}: S={spec.num_seqs} T={spec.num_tokens} q={[int(x) for x in spec.q_lens]} "
+         f"ctx={[int(x) for x in spec.ctx_lens]} Hq/Hkv/D/B={spec.num_q_heads}/{spec.num_kv_heads}/"
+         f"{spec.head_dim}/{spec.block_size} {knobs}")
+    tens, _, _, out, lse, plan = G.full_gpu_pass(spec, **knobs)
+    check_plan(plan, spec)
+    o_ref, l_ref = G.oracle_pass(spec, tens)
+    compare(out, lse, o_ref, l_ref, f"random {seed}")
+
+
 @pytest.mark.parametrize("name", ["tiny", "mha_d128_b64_mixed", "gqa8_d128_b64_mixed", "gqa4_d64_b16_mixed"])
 def test_append_is_bit_exact(name):
     spec = SMALL_SPECS[name]()

@@ -96,6 +96,13 @@ def test_skewed_decode_only_pass_splits_only_its_longest_decodes():
     assert (per_seq[kv * 1.0 <= half_target] == 1).all()
 
 
+@pytest.mark.parametrize("seed", range(40))
+def test_random_compositions_cover_every_row_once(seed):
+    from tests._random_passes import random_pass
+    spec, knobs = random_pass(seed)
+    check_plan(plan_of(spec, **knobs), spec)
+
+
 def _item_costs(items):
     lengths = (items[:, 5] - items[:, 4]).astype(np.float64)
     mf = items[:, 7] > 0
