@@ -690,6 +690,7 @@ def main():
                 "hbm": round(attn_gbs / achievable["hbm_gbs"], 4),
                 "mfma": round(attn_tflops / achievable["bf16_gemm_tflops"], 4)} if achievable else None,
             "kernel_source_sha256_16": source_hash(),
+            "kernel_events": args.kernel_events,
         },
     }
     if args.copy_probe_mib > 0:
