@@ -110,7 +110,10 @@ def gather_sequence(k_pool, v_pool, table_row, length, block_size):
     """Read positions 0..length-1 of one sequence back out of the pools.
 
     Walks the block table (a read path, separate from kv_append's write path)
-    and returns K and V as [length, Hkv, D] in logical position order.
+    and returns K and V as [length, Hkv, D] in logical position order: logical
+    position p lives in block table_row[p // block_size] at slot
+    p % block_size (FastGen Guide, section "3. Paged KV Memory Management with
+    Zero Overhead").
     """
     nblk = -(-int(length) // block_size)
     ids = np.asarray(table_row[:nblk], dtype=np.int64)
@@ -224,7 +227,9 @@ def attend_split(q, k_pool, v_pool, q_lens, ctx_lens, block_tables, block_size,
 
     ``ranges_for(s, length)`` returns the list of [k0, k1) ranges that
     partition [0, length) for sequence s.  Each range yields a partial via
-    partial_attend and the partials are merged by ``merge``.
+    partial_attend and the partials are merged by ``merge``: the two-phase
+    split-KV computation of the FastGen Guide, section "1. Dynamic SplitKV
+    Attention", and its Step 3 code.
     """
     t_tot, hq, d = q.shape
     group = hq // num_kv_heads
