@@ -88,3 +88,22 @@ def test_profile_mask_toggles_without_a_device():
     binding.fg_profile_enable(False)
     lib = binding.lib()
     assert lib.fg_profile_read(None, None, -1) == binding.FG_E_INVALID
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """No fallback path: with the library absent, the first call raises."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("from ragged_paged_attention_splitfuse_amd import binding\n"
+            "try:\n"
+            "    binding.fg_abi_version()\n"
+            "except binding.FgError as e:\n"
+            "    print('raised', e)\n"
+            "else:\n"
+            "    print('no error')\n")
+    env = dict(os.environ, FG_LIBRARY=str(tmp_path / "absent" / "libfg.so"))
+    res = subprocess.run([sys.executable, "-c", code], cwd=root, env=env, capture_output=True,
+                         text=True, timeout=120)
+    assert res.returncode == 0, res.stderr
+    assert res.stdout.startswith("raised") and "not built" in res.stdout, res.stdout
