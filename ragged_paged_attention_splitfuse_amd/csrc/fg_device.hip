@@ -182,15 +182,18 @@ __device__ __forceinline__ float load_partial(const float* p) {
 
 // ----------------------------------------------------------------------------
 // Vector-ALU path: up to NR query rows of one (sequence, kv head) over the
-// item's KV range.  Wavefront w handles 32-token sub-tiles w, w+4, w+8, ...
-// with its own online-softmax state; the four states merge at the end.
+// item's KV range.  Wavefront w handles ST-token steps w, w+4, w+8, ...
+// (ST = 32 or 64: one or two 32-token V^T sub-blocks) with its own
+// online-softmax state; the four states merge at the end.
 // LDS use: per-wave probability exchange, then the cross-wave merge buffers.
-template <int D, int B, int NR>
+template <int D, int B, int NR, int ST>
 __device__ void valu_item(const AttnArgs& a, const ItemRec& it, float* smem) {
+  static_assert(ST % kValuSubTile == 0 && kKvTile % ST == 0, "whole sub-blocks per step");
   constexpr int LPT = D / 8;                // lanes holding one 16-byte-chunked K row
   constexpr int TPI = 64 / LPT;             // tokens per K load instruction
-  constexpr int UK = kValuSubTile / TPI;    // K loads per sub-tile
-  constexpr int UV = D / 16;                // V^T loads per sub-tile (16 dims each)
+  constexpr int HV = ST / kValuSubTile;     // 32-token V^T sub-blocks per step
+  constexpr int UK = ST / TPI;              // K loads per step
+  constexpr int UV = D / 16;                // V^T loads per half (16 dims each)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const SeqRec sq = a.seqs[it.seq];
   const int32_t* bt = a.bt + sq.bt_off;
@@ -220,36 +223,39 @@ __device__ void valu_item(const AttnArgs& a, const ItemRec& it, float* smem) {
 #pragma unroll
     for (int i = 0; i < UV; ++i) acc[r][i] = 0.f;
   }
-  float* pbuf = smem + wave * (NR * kValuSubTile);
+  float* pbuf = smem + wave * (NR * ST);
 
-  for (int t0 = it.kv0 + wave * kValuSubTile; t0 < it.kv1; t0 += kWaves * kValuSubTile) {
-    u32x4 kr[UK], vr[UV];
+  for (int t0 = it.kv0 + wave * ST; t0 < it.kv1; t0 += kWaves * ST) {
+    u32x4 kr[UK], vr[HV][UV];
     int blk_u = 0;
-    if constexpr (B >= kValuSubTile) blk_u = bt[t0 / B];
+    if constexpr (B >= ST) blk_u = bt[t0 / B];
 #pragma unroll
     for (int i = 0; i < UK; ++i) {
       const int tok = t0 + i * TPI + ktok;
       kr[i] = u32x4{0u, 0u, 0u, 0u};
       if (tok < kv_valid) {
-        const int blk = (B >= kValuSubTile) ? blk_u : bt[tok / B];
+        const int blk = (B >= ST) ? blk_u : bt[tok / B];
         // Each K and V^T load instruction reads whole 128-byte lines (TPI full
         // K rows; 16 dims of one V^T sub-block) that no other load of this
         // item touches again, so both stream with the non-temporal hint.
         kr[i] = ld16_nt(a.kpool + ((size_t(blk) * a.hkv + g) * B + tok % B) * D + 8 * kdc);
       }
     }
-    const int vt = t0 + 8 * vtc;
 #pragma unroll
-    for (int i = 0; i < UV; ++i) {
-      vr[i] = u32x4{0u, 0u, 0u, 0u};
-      if (vt < kv_valid) {
-        const int blk = (B >= kValuSubTile) ? blk_u : bt[vt / B];
-        vr[i] = ld16_nt(a.vpool + (size_t(blk) * a.hkv + g) * D * B + vt_off<D, B>(vd + 16 * i, vt % B));
+    for (int h = 0; h < HV; ++h) {
+      const int vt = t0 + kValuSubTile * h + 8 * vtc;
+#pragma unroll
+      for (int i = 0; i < UV; ++i) {
+        vr[h][i] = u32x4{0u, 0u, 0u, 0u};
+        if (vt < kv_valid) {
+          const int blk = (B >= ST) ? blk_u : bt[vt / B];
+          vr[h][i] = ld16_nt(a.vpool + (size_t(blk) * a.hkv + g) * D * B + vt_off<D, B>(vd + 16 * i, vt % B));
+        }
       }
-    }
-    if (vt < kv_valid && vt + 8 > kv_valid) {
+      if (vt < kv_valid && vt + 8 > kv_valid) {
 #pragma unroll
-      for (int i = 0; i < UV; ++i) vr[i] = zero_tail(vr[i], vt, kv_valid);
+        for (int i = 0; i < UV; ++i) vr[h][i] = zero_tail(vr[h][i], vt, kv_valid);
+      }
     }
 
     // scores (log2 units), masked by range and causal limit
@@ -293,36 +299,43 @@ __device__ void valu_item(const AttnArgs& a, const ItemRec& it, float* smem) {
 #pragma unroll
       for (int r = 0; r < NR; ++r)
 #pragma unroll
-        for (int i = 0; i < UK; ++i) pbuf[r * kValuSubTile + i * TPI + ktok] = s[r][i];
+        for (int i = 0; i < UK; ++i) pbuf[r * ST + i * TPI + ktok] = s[r][i];
     }
     __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    float pp[NR][8];
+    float pp[HV][NR][8];
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      const f32x4 x0 = *reinterpret_cast<const f32x4*>(pbuf + r * kValuSubTile + 8 * vtc);
-      const f32x4 x1 = *reinterpret_cast<const f32x4*>(pbuf + r * kValuSubTile + 8 * vtc + 4);
+    for (int h = 0; h < HV; ++h)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pp[r][e] = x0[e];
-        pp[r][4 + e] = x1[e];
+      for (int r = 0; r < NR; ++r) {
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(pbuf + r * ST + kValuSubTile * h + 8 * vtc);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(pbuf + r * ST + kValuSubTile * h + 8 * vtc + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pp[h][r][e] = x0[e];
+          pp[h][r][4 + e] = x1[e];
+        }
       }
-    }
     __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 
 #pragma unroll
     for (int i = 0; i < UV; ++i) {
-      float v[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[2 * e] = bf_lo(vr[i][e]);
-        v[2 * e + 1] = bf_hi(vr[i][e]);
-      }
+      for (int r = 0; r < NR; ++r) acc[r][i] *= alpha[r];
 #pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        float t = acc[r][i] * alpha[r];
+      for (int h = 0; h < HV; ++h) {
+        float v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) t = fmaf(pp[r][u], v[u], t);
-        acc[r][i] = t;
+        for (int e = 0; e < 4; ++e) {
+          v[2 * e] = bf_lo(vr[h][i][e]);
+          v[2 * e + 1] = bf_hi(vr[h][i][e]);
+        }
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          float t = acc[r][i];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) t = fmaf(pp[h][r][u], v[u], t);
+          acc[r][i] = t;
+        }
       }
     }
   }
@@ -342,7 +355,7 @@ __device__ void valu_item(const AttnArgs& a, const ItemRec& it, float* smem) {
   }
 
   // cross-wavefront log-sum-exp merge
-  float* ms = smem + kWaves * NR * kValuSubTile;
+  float* ms = smem + kWaves * NR * ST;
   float* ls = ms + kWaves * NR;
   float* as = ls + kWaves * NR;
   if (lane == 0) {
@@ -702,10 +715,9 @@ __device__ void mfma_item(const AttnArgs& a, const ItemRec& it, uint16_t* lds) {
   }
 }
 
-template <int D>
+template <int D, int ST>
 constexpr int valu_lds_bytes() {
-  return (kWaves * kValuMaxRows * kValuSubTile + 2 * kWaves * kValuMaxRows +
-          kWaves * kValuMaxRows * D) * 4;
+  return (kWaves * kValuMaxRows * ST + 2 * kWaves * kValuMaxRows + kWaves * kValuMaxRows * D) * 4;
 }
 
 // Log-sum-exp merge of one split group (every row, every split), by the whole
@@ -815,11 +827,16 @@ __device__ void finish_split(const AttnArgs& a, const ItemRec& it, int* last_fla
     __hip_atomic_store(a.counters + it.group, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The decode loop's step: in the kernel that also runs matrix-core tiles the
+// tile path sets the register budget, and 64-token steps (twice the loads in
+// flight per wavefront) fit inside it; the decode-only kernel keeps 32-token
+// steps, whose smaller register count lets a CU hold a third work-group.
 template <int D, int B, bool MFMA>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
-  constexpr int kLds = MFMA ? (MfmaLds<D>::BYTES > valu_lds_bytes<D>() ? MfmaLds<D>::BYTES
-                                                                        : valu_lds_bytes<D>())
-                            : valu_lds_bytes<D>();
+  constexpr int kStep = MFMA ? 2 * kValuSubTile : kValuSubTile;
+  constexpr int kLds = MFMA ? (MfmaLds<D>::BYTES > valu_lds_bytes<D, kStep>() ? MfmaLds<D>::BYTES
+                                                                               : valu_lds_bytes<D, kStep>())
+                            : valu_lds_bytes<D, kStep>();
   __shared__ __attribute__((aligned(16))) unsigned char smem[kLds];
   const ItemRec it = a.items[blockIdx.x];
   if constexpr (MFMA) {
@@ -830,9 +847,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
     }
   }
   if (it.nrows == 1)
-    valu_item<D, B, 1>(a, it, reinterpret_cast<float*>(smem));
+    valu_item<D, B, 1, kStep>(a, it, reinterpret_cast<float*>(smem));
   else
-    valu_item<D, B, kValuMaxRows>(a, it, reinterpret_cast<float*>(smem));
+    valu_item<D, B, kValuMaxRows, kStep>(a, it, reinterpret_cast<float*>(smem));
   if (it.group >= 0 && it.group < a.n_inlaunch) finish_split<D>(a, it, reinterpret_cast<int*>(smem));
 }
 

@@ -16,7 +16,8 @@ constexpr int kMfmaTileRows = kMfmaRowsPerWave * kMfmaMaxWaves;
 // KV tokens per LDS stage on the matrix-core path; split boundaries are
 // aligned to it so every item starts on a stage boundary.
 constexpr int kKvTile = 64;
-// KV tokens per wavefront step on the vector-ALU path (divides kKvTile).
+// KV tokens per V^T sub-block, and per vector-ALU wavefront step in the
+// decode-only kernel (the mixed kernel steps two at a time); divides kKvTile.
 constexpr int kValuSubTile = 32;
 
 // Per-sequence record.
