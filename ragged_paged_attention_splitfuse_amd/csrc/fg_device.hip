@@ -13,7 +13,7 @@
 //                   O^T = V^T P^T on v_mfma_f32_32x32x16_bf16, online softmax in
 //                   fp32 with one query row per lane.  Items with at most four
 //                   rows (decodes) take the vector-ALU path: every wavefront
-//                   streams its own 32-token sub-tiles with 16-byte loads,
+//                   streams its own 32- or 64-token steps with 16-byte loads,
 //                   dot products on v_dot2_f32_bf16 with DPP row reductions, and
 //                   the four wavefronts merge by log-sum-exp at the end.
 //                   An item that is one split of a longer KV range writes its
