@@ -91,6 +91,22 @@ def test_random_compositions_match_oracle(seed):
     compare(out, lse, o_ref, l_ref, f"random {seed}")
 
 
+# FG_RANDOM_BIG_CASES widens this one too (for example 400).
+RANDOM_BIG_CASES = int(os.environ.get("FG_RANDOM_BIG_CASES", "8"))
+
+
+@pytest.mark.parametrize("seed", range(RANDOM_BIG_CASES))
+def test_random_big_compositions_match_oracle(seed):
+    from tests._random_passes import random_big_pass
+    spec, knobs = random_big_pass(seed)
+    _log(f"[case] random big {seed}: S={spec.num_seqs} T={spec.num_tokens} max ctx={int(max(spec.ctx_lens))} "
+         f"Hq/Hkv/D/B={spec.num_q_heads}/{spec.num_kv_heads}/{spec.head_dim}/{spec.block_size} {knobs}")
+    tens, _, _, out, lse, plan = G.full_gpu_pass(spec, **knobs)
+    check_plan(plan, spec)
+    o_ref, l_ref = G.oracle_pass(spec, tens)
+    compare(out, lse, o_ref, l_ref, f"random big {seed}")
+
+
 @pytest.mark.parametrize("name", ["tiny", "mha_d128_b64_mixed", "gqa8_d128_b64_mixed", "gqa4_d64_b16_mixed"])
 def test_append_is_bit_exact(name):
     spec = SMALL_SPECS[name]()
