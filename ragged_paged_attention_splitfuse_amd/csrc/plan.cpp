@@ -43,6 +43,14 @@ constexpr int kMaxSplitsLimit = 256;
 // balance and costs partial-row traffic plus the merge (measured on the 7B
 // 2048-token pass: 256 us per pass at 2, 280 us at 3 and 4).
 constexpr double kItemsPerCu = 2.0;
+// A pass whose groups all take the matrix-core path (GQA groups of more than
+// kValuMaxRows rows) is split more coarsely: its items carry several query
+// rows per KV stream, and each split adds a partial write and a merge for all
+// of them.  Measured on the 70B GQA passes (16/2 heads): the 32-decode half
+// 31.7 -> 29.4 us of attention, the 4096-token share 104 -> 102 us; at 1.0 the
+// share lost (117 us).  Passes with vector-ALU decodes stay at kItemsPerCu
+// (the 7B decode half: 117 us at 2.0, 127 us at 1.5).
+constexpr double kMfmaOnlyItemsPerCu = 1.5;
 // Matrix-core tiles: relative cost per KV token of a tile with R padded rows
 // is max(kMfmaMinCost, R / kFlopPerByte), where kFlopPerByte is the ratio of
 // achievable bf16 MFMA rate to achievable HBM rate on MI355X (about
@@ -307,20 +315,23 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
     }
 
     // ---- split each group's visible range [0, vis_end)
-    int64_t tile_groups = 0;
+    int64_t tile_groups = 0, valu_groups = 0;
     double tile_cost = 0.0;
-    for (const Group& grp : groups)
+    for (const Group& grp : groups) {
+      if (grp.waves == 0) ++valu_groups;
       if (grp.waves >= 2) {
         ++tile_groups;
         tile_cost += grp.cost;
       }
+    }
+    const double items_per_cu = valu_groups == 0 ? kMfmaOnlyItemsPerCu : kItemsPerCu;
     // A pass of vector-ALU groups only, with at least kSkewedItemsPerSlot of
     // them per work-group slot, halves the split target (see kSkewedSplitFactor).
     const bool many_valu_groups =
         tile_groups == 0 &&
         double(groups.size()) >= kSkewedItemsPerSlot * double(target_cus) * kMfmaSlotsPerCu;
     const double target = std::max(
-        1.0, total_cost / (double(target_cus) * kItemsPerCu * (many_valu_groups ? kSkewedSplitFactor : 1.0)));
+        1.0, total_cost / (double(target_cus) * items_per_cu * (many_valu_groups ? kSkewedSplitFactor : 1.0)));
     const double tile_target =
         tile_groups >= target_cus
             ? 1e300
