@@ -84,6 +84,45 @@ def test_append_places_every_element_by_its_flat_address(b):
     assert np.count_nonzero(vf != canary) == t * hkv * d
 
 
+@pytest.mark.parametrize("b", [4, 16, 32, 64])
+def test_gather_reads_every_element_from_its_flat_address(b):
+    # Read-side mirror of the append pin: pools are filled directly, element by
+    # element at the flat address the layout defines (K [blk][g][slot][e]; V
+    # [blk][g][slot // S][e][slot % S], S = min(b, 32)), with a value that
+    # names (sequence, position, head, dim).  gather_sequence must return them
+    # in logical position order, so any index mix-up in its read path (block,
+    # sub-block, slot, head or dim) shows.
+    hkv, d = 2, 8
+    lengths = [2 * b + 7, 1, b + 1]
+    spec = _tiny_spec([1, 1, 1], [n - 1 for n in lengths], hq=hkv, hkv=hkv, d=d, b=b, nb=12)
+    sub = min(b, 32)
+    kf = np.full(spec.num_blocks * hkv * b * d, 0xFFFF, np.uint16)
+    vf = np.full(spec.num_blocks * hkv * b * d, 0xFFFF, np.uint16)
+
+    def ident(s, p, g, e, which):
+        return ((which * 4 + s) * 256 + p) * 16 + g * d + e   # < 2**16, unique
+
+    for s, n in enumerate(lengths):
+        for p in range(n):
+            blk = int(spec.block_tables[s][p // b])
+            off = p % b
+            for g in range(hkv):
+                for e in range(d):
+                    kf[((blk * hkv + g) * b + off) * d + e] = ident(s, p, g, e, 0)
+                    vf[(blk * hkv + g) * d * b + (off // sub) * (d * sub) + e * sub + off % sub] = \
+                        ident(s, p, g, e, 1)
+    kp = kf.reshape(spec.num_blocks, hkv, b, d)
+    vp = vf.reshape(spec.num_blocks, hkv, b // sub, d, sub)
+    for s, n in enumerate(lengths):
+        k, v = ora.gather_sequence(kp, vp, spec.block_tables[s], n, b)
+        assert k.shape == (n, hkv, d) and v.shape == (n, hkv, d)
+        for p in range(n):
+            for g in range(hkv):
+                for e in range(d):
+                    assert k[p, g, e] == ident(s, p, g, e, 0), ("K", s, p, g, e)
+                    assert v[p, g, e] == ident(s, p, g, e, 1), ("V", s, p, g, e)
+
+
 # ---------------------------------------------------------------- reference reductions
 
 def _run(spec, poison=False, scale=None):
@@ -126,14 +165,28 @@ def test_textbook_reduction_single_contiguous_sequence():
     assert np.max(np.abs(lse - l_ref)) <= 1e-12
 
 
-@pytest.mark.parametrize("cfg", [1, "mixed_gqa"])
-def test_dense_library_reference_ragged_paged(cfg):
+DENSE_REFERENCE_SPECS = {
+    "tiny": lambda: wl.config_spec(1),
+    "mixed_gqa_b16": lambda: _tiny_spec([17, 1, 1, 33, 2], [0, 50, 7, 21, 63], hq=8, hkv=2, d=64,
+                                        b=16, seed=5),
+    # B = 32: one V sub-block per block; chunks cross block boundaries.
+    "mixed_mha_b32": lambda: _tiny_spec([40, 1, 17, 3], [0, 50, 20, 61], hq=4, hkv=4, d=16, b=32,
+                                        seed=42),
+    # B = 64: two V sub-blocks per block.  Sequence 0 (70 tokens at ctx 0)
+    # fills both sub-blocks of its first block; sequence 3 appends positions
+    # 90..122, across the sub-block boundary at 96; sequence 4 crosses the
+    # block boundary at 64; the decodes sit at 100 and 63 (a sub-block's last
+    # slot and a block's last slot).
+    "mixed_gqa_b64": lambda: _tiny_spec([70, 1, 1, 33, 5], [0, 100, 63, 90, 60], hq=4, hkv=2, d=32,
+                                        b=64, seed=41),
+}
+
+
+@pytest.mark.parametrize("name", sorted(DENSE_REFERENCE_SPECS))
+def test_dense_library_reference_ragged_paged(name):
     # Shuffled blocks, nonzero ctx, GQA: the oracle's append + gather + attend
     # against SDPA on the logical (never paged) K/V arrays.
-    if cfg == "mixed_gqa":
-        spec = _tiny_spec([17, 1, 1, 33, 2], [0, 50, 7, 21, 63], hq=8, hkv=2, d=64, b=16, seed=5)
-    else:
-        spec = wl.config_spec(1)
+    spec = DENSE_REFERENCE_SPECS[name]()
     tens, _, _, o, lse = _run(spec, poison=True)
     o_ref, l_ref = _torch_reference(spec, tens, 1 / math.sqrt(spec.head_dim))
     assert np.max(np.abs(o - o_ref)) <= 1e-12
@@ -243,19 +296,29 @@ def test_two_key_weights_quarter_three_quarters():
 
 # ---------------------------------------------------------------- addressing probe
 
-def test_one_hot_probe_every_block_boundary():
+ONE_HOT_SPECS = {
+    "tiny_b16": lambda: wl.config_spec(1),
+    "mixed_b32": lambda: _tiny_spec([40, 1, 9], [0, 70, 60], hq=4, hkv=4, d=64, b=32, seed=43),
+    "mixed_b64": lambda: _tiny_spec([70, 1, 40], [0, 130, 90], hq=4, hkv=4, d=64, b=64, seed=44),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ONE_HOT_SPECS))
+def test_one_hot_probe_every_block_boundary(name):
     # q = 32 e0 and a single key with k[0] = 32: score 1024 / sqrt(64) = 128
     # against 0 for every other key, so exp(-128) ~ 2.6e-56 and O is V[t*]
     # to far below 1e-40.  The probe is swept over both sides of every block
-    # boundary of every sequence, in a shuffled pool.
-    spec = wl.config_spec(1)
+    # boundary of every sequence (and of every 32-slot V sub-block boundary
+    # inside 64-slot blocks), in a shuffled pool.
+    spec = ONE_HOT_SPECS[name]()
     b = spec.block_size
+    sub = min(b, 32)
     base = wl.make_tensors(spec)
     cu = cu_seqlens(spec.q_lens)
     for s in range(spec.num_seqs):
         c, n = int(spec.ctx_lens[s]), int(spec.q_lens[s])
         length = c + n
-        targets = sorted({t for blk in range(-(-length // b)) for t in (blk * b, blk * b + b - 1)
+        targets = sorted({t for blk in range(-(-length // sub)) for t in (blk * sub, blk * sub + sub - 1)
                           if t < length})
         for tstar in targets:
             tens = wl.PassTensors(q=np.zeros_like(base.q), k_new=np.zeros_like(base.k_new),
