@@ -34,6 +34,14 @@ using fg::SeqRec;
 
 constexpr int64_t kMaxTokens = int64_t(1) << 28;
 constexpr int64_t kMaxKvLen = int64_t(1) << 28;
+// Every launch runs 256-thread work-groups and a dispatch's work-item count
+// is a 32-bit number, so one launch holds at most 2^24 - 1 work-groups: the
+// attention items, the merge groups, and the append launch's (run, kv head)
+// pairs plus its metadata-copy groups.  Packed query rows of a (sequence, kv
+// head), q_len * G, are int32 indices in the item records.  Passes past
+// either limit are rejected with FG_E_RANGE before anything is sized by them.
+constexpr int64_t kMaxGroupsPerLaunch = (int64_t(1) << 24) - 1;
+constexpr int64_t kMaxPackedRows = INT32_MAX;
 constexpr int kDefaultMinSplitTokens = 256;
 constexpr int kDefaultMaxSplits = 64;
 constexpr int kMaxSplitsLimit = 256;
@@ -222,6 +230,16 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
       used_blocks += nblk;
       if (tokens > kMaxTokens) return FG_E_RANGE;
     }
+    // Packed rows per (sequence, kv head) and the row-group count, in 64-bit
+    // arithmetic, before any vector is sized by them.
+    int64_t group_count = 0;
+    for (int s = 0; s < S; ++s) {
+      const int64_t rows = int64_t(seqs[s].q_len) * G;
+      if (rows > kMaxPackedRows) return FG_E_RANGE;
+      const int64_t per_head = rows <= fg::kValuMaxRows ? 1 : ceil_div(rows, fg::kMfmaTileRows);
+      group_count += per_head * d->num_kv_heads;
+      if (group_count > kMaxGroupsPerLaunch) return FG_E_RANGE;
+    }
     std::vector<int32_t> bt(static_cast<size_t>(used_blocks));
     std::vector<uint8_t> seen(size_t(d->num_blocks), 0);
     for (int s = 0; s < S; ++s) {
@@ -261,16 +279,17 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
         p = end;
       }
     }
+    if (int64_t(runs.size()) * d->num_kv_heads > kMaxGroupsPerLaunch) return FG_E_RANGE;
 
     // ---- row groups and their costs (KV tokens visible to the group: a
     // decode group streams them from HBM, a full 128-row tile spends about the
     // same time on matrix-core work per token at the MI355X flop:byte ratio)
     std::vector<Group> groups;
-    groups.reserve(size_t(S) * size_t(d->num_kv_heads) * 2);
+    groups.reserve(size_t(group_count));
     double total_cost = 0.0;
     for (int s = 0; s < S; ++s) {
       const SeqRec& r = seqs[s];
-      const int rows = r.q_len * G;
+      const int rows = int(int64_t(r.q_len) * G);   // <= kMaxPackedRows, checked above
       for (int g = 0; g < d->num_kv_heads; ++g) {
         if (rows <= fg::kValuMaxRows) {
           Group grp{s, g, 0, rows, r.kv_len, 0, double(r.kv_len)};
@@ -371,6 +390,7 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
       return items;
     };
     int64_t total_items = split_all(target);
+    if (total_items > kMaxGroupsPerLaunch) return FG_E_RANGE;
     // Round fitting (see kRoundFitSlack): a tile-free plan just past a whole
     // number of work-group rounds gets a larger target until it fits them.
     if (d->force_splits == 0 && d->split_policy == FG_SPLIT_BALANCED && tile_groups == 0) {
@@ -381,7 +401,7 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
         const int64_t excess = total_items - rounds * slots;
         if (rounds < 1 || excess == 0 || double(excess) > kRoundFitSlack * double(slots)) break;
         valu_target *= double(total_items) / double(rounds * slots);
-        total_items = split_all(valu_target);
+        total_items = split_all(valu_target);   // a larger target: never more items
       }
     }
     const bool inlaunch_ok =
@@ -481,6 +501,13 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
     plan->off_items = off;  off = align16(off + sizeof(ItemRec) * size_t(plan->n_items));
     plan->off_merges = off; off = align16(off + sizeof(MergeRec) * merges.size());
     plan->off_counters = off; off = align16(off + sizeof(int32_t) * size_t(n_inl));
+    // the fused upload + append launch: metadata-copy groups of 4 KiB each
+    // beside the (run, kv head) groups
+    if (int64_t(ceil_div(int64_t(off), 4096)) + int64_t(runs.size()) * d->num_kv_heads >
+        kMaxGroupsPerLaunch) {
+      delete plan;
+      return FG_E_RANGE;
+    }
     plan->blob.assign(std::max<size_t>(off, 16), 0);
     uint8_t* base = plan->blob.data();
     if (!seqs.empty()) memcpy(base + plan->off_seqs, seqs.data(), sizeof(SeqRec) * seqs.size());

@@ -240,3 +240,27 @@ def test_engine_policy_golden_case():
     plan = plan_of(spec, target_cus=108, split_policy=fgb.FG_SPLIT_ENGINE,
                    min_split_tokens=512, max_splits=256)
     assert _splits_per_seq(plan, 4) == [_aligned(k, L) for k, L in zip([4, 8, 32, 64], lens)]
+
+
+@pytest.mark.parametrize("q_len,hq,hkv", [
+    (65536, 65536, 1),      # q_len * G = 2^32 packed rows: past int32
+    (32768, 65536, 1),      # 2^31 packed rows: one past INT32_MAX
+    (16384, 16384 * 16, 16),  # 2^28 rows per kv head, 2^25 row tiles: past one launch
+])
+def test_rows_and_launch_sizes_past_the_limits_are_rejected(q_len, hq, hkv):
+    # A plan that exists is valid: packed row indices are int32 and a launch
+    # holds at most 2^24 - 1 work-groups, so larger passes return FG_E_RANGE
+    # instead of wrapping around.
+    b = 64
+    bt = np.arange(-(-q_len // b), dtype=np.int32).reshape(1, -1)
+    with pytest.raises(fgb.FgError) as e:
+        fgb.Plan([q_len], [0], bt, hq, hkv, 128, b, bt.size, target_cus=64)
+    assert e.value.status == fgb.FG_E_RANGE
+
+
+def test_large_but_valid_gqa_chunk_is_planned():
+    # 8192 rows per kv head (q_len 1024, G 8): inside every limit
+    b = 64
+    spec = wl.custom_spec("g", [1024, 1], [0, 700], 16, 2, 128, b, seed=9)
+    plan = plan_of(spec)
+    check_plan(plan, spec)
