@@ -123,11 +123,12 @@ typedef struct fg_pass_desc {
  *                      balanced over target_cus compute units.
  *   FG_SPLIT_ENGINE    per sequence, the allocation engine of "DeepSpeed-FastGen
  *                      Guide: Dynamic SplitKV Serving", section "Step 2: Dynamic
- *                      SplitKV Allocation Engine": no split at or below
- *                      min_split_tokens (default 256), else kv_len /
- *                      min_split_tokens capped at 16, then every count scaled by
- *                      target_cus / total when the total is smaller, and all
- *                      ones when there are at least target_cus sequences.
+ *                      SplitKV Allocation Engine", as a formula: with
+ *                      N = target_cus, m = min_split_tokens (default 256),
+ *                      b_s = clamp(kv_len_s / m, 1, 16) and B = sum of b_s,
+ *                      k_s = 1 when there are at least N sequences, else
+ *                      max(1, b_s * N / B) when B < N, else b_s (integer
+ *                      floors; the scaled count may exceed 16).
  *   FG_SPLIT_PER_1K    per sequence, kv_len / 1024 clamped to [1, 16]: the
  *                      reading of the same page's figure "Dynamic SplitKV
  *                      Two-Phase Attention Kernel Workflow" (512, 4096 and 16384

@@ -5,46 +5,43 @@ this module.  These policies decide only how many KV splits each sequence
 gets; attention results do not depend on them (any partition merges to the
 same output), so they matter for speed alone.
 
-Two policies are printed on "DeepSpeed-FastGen Guide: Dynamic SplitKV
-Serving" and they disagree with each other:
+Both are stated as per-sequence formulas over the context lengths L_s of the
+S sequences of a pass, and implemented as such (whole-array arithmetic, exact
+integer floors).  They come from "DeepSpeed-FastGen Guide: Dynamic SplitKV
+Serving", and they disagree with each other:
 
-* ``host_heuristic`` restates the allocation engine of section "Step 2:
-  Dynamic SplitKV Allocation Engine": no split at or below a minimum chunk,
-  otherwise one split per minimum chunk capped at 16, then every count is
-  scaled up by (SM count / total) when the total falls short of the SM count,
-  and everything collapses to one split when there are at least as many
-  sequences as SMs.  Note that the scaling step can push a count past its own
-  cap of 16.
-* ``figure_rule`` reproduces the worked example of the figure "Dynamic
-  SplitKV Two-Phase Attention Kernel Workflow" (512, 4096 and 16384 tokens get
-  1, 4 and 16 splits).  The figure prints only the outcome; the reading taken
-  here is one split per 1024 tokens, at least 1 and at most 16, with no SM
-  scaling -- the plainest rule that gives the printed numbers.
+* ``engine_counts``: the allocation engine of section "Step 2: Dynamic
+  SplitKV Allocation Engine", with N compute units and a minimum chunk of m
+  tokens.  Every sequence gets one split when S >= N.  Otherwise a base count
+  b_s = min(16, max(1, floor(L_s / m))) is scaled up so that the counts come
+  to about N: with B = sum_s b_s, k_s = max(1, floor(b_s * N / B)) when
+  B < N, else k_s = b_s.  The scaled count can exceed the base cap of 16.
+  The page's code multiplies by N / B in floating point, which can land one
+  below an exact integer (11 * (15 / 11) gives 14.999...); the formula is
+  read with exact arithmetic.
+* ``figure_counts``: the worked example of the figure "Dynamic SplitKV
+  Two-Phase Attention Kernel Workflow" (512, 4096 and 16384 tokens get 1, 4
+  and 16 splits).  The figure prints only the outcome; the reading taken here
+  is k_s = min(16, max(1, floor(L_s / 1024))), the plainest rule that gives
+  the printed numbers, with no compute-unit scaling.
 """
+import numpy as np
 
-__all__ = ["host_heuristic", "figure_rule"]
+__all__ = ["engine_counts", "figure_counts"]
 
 
-def host_heuristic(seq_lengths, num_sms=108, min_chunk_size=256):
+def engine_counts(seq_lengths, num_sms=108, min_chunk_size=256):
     """Split counts per sequence under the Step 2 allocation engine."""
-    n = len(seq_lengths)
-    if n == 0:
-        return []
-    if n >= num_sms:
-        return [1] * n
-    counts = []
-    for length in seq_lengths:
-        if length <= min_chunk_size:
-            counts.append(1)
-        else:
-            counts.append(min(max(1, length // min_chunk_size), 16))
-    total = sum(counts)
-    if total < num_sms:
-        factor = num_sms / total
-        counts = [max(1, int(c * factor)) for c in counts]
-    return counts
+    lengths = np.asarray(seq_lengths, dtype=np.int64)
+    if lengths.size >= num_sms:
+        return [1] * int(lengths.size)
+    base = np.clip(lengths // min_chunk_size, 1, 16)
+    total = int(base.sum())
+    counts = np.maximum(1, (base * num_sms) // total) if 0 < total < num_sms else base
+    return [int(k) for k in counts]
 
 
-def figure_rule(seq_lengths, tokens_per_split=1024, cap=16):
+def figure_counts(seq_lengths, tokens_per_split=1024, cap=16):
     """Split counts per sequence under the workflow figure's worked example."""
-    return [min(max(1, length // tokens_per_split), cap) for length in seq_lengths]
+    lengths = np.asarray(seq_lengths, dtype=np.int64)
+    return [int(k) for k in np.clip(lengths // tokens_per_split, 1, cap)]

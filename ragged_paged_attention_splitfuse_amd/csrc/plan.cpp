@@ -312,25 +312,24 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
     }
 
     // ---- per-sequence split counts of the pages' policies (FG_SPLIT_ENGINE,
-    // FG_SPLIT_PER_1K; see fg.h), from each sequence's KV length
+    // FG_SPLIT_PER_1K; see fg.h), as per-sequence formulas of the KV length:
+    //   engine:  b_s = clamp(L_s / m, 1, 16), B = sum b_s over the pass;
+    //            k_s = 1 if S >= N, else max(1, b_s * N / B) if B < N, else b_s
+    //   per 1k:  k_s = clamp(L_s / 1024, 1, 16)
+    // (N = target_cus, m = min_split_tokens or 256; integer floors throughout)
     std::vector<int64_t> seq_splits(size_t(S), 1);
-    if (d->split_policy == FG_SPLIT_ENGINE && S > 0) {
-      const int64_t chunk_min = d->min_split_tokens > 0 ? d->min_split_tokens : kDefaultMinSplitTokens;
-      if (S < target_cus) {
-        int64_t total = 0;
-        for (int s = 0; s < S; ++s) {
-          const int64_t len = seqs[s].kv_len;
-          seq_splits[size_t(s)] = len <= chunk_min ? 1 : std::min<int64_t>(std::max<int64_t>(1, len / chunk_min), 16);
-          total += seq_splits[size_t(s)];
-        }
-        if (total < target_cus) {
-          const double factor = double(target_cus) / double(total);
-          for (int64_t& k : seq_splits) k = std::max<int64_t>(1, int64_t(double(k) * factor));
-        }
+    if (d->split_policy == FG_SPLIT_ENGINE) {
+      const int64_t m = d->min_split_tokens > 0 ? d->min_split_tokens : kDefaultMinSplitTokens;
+      int64_t base_sum = 0;
+      for (int s = 0; s < S; ++s) {
+        seq_splits[size_t(s)] = std::clamp<int64_t>(seqs[s].kv_len / m, 1, 16);
+        base_sum += seq_splits[size_t(s)];
       }
+      const int64_t n_cus = target_cus;
+      for (int64_t& k : seq_splits)
+        k = S >= n_cus ? 1 : base_sum < n_cus ? std::max<int64_t>(1, k * n_cus / base_sum) : k;
     } else if (d->split_policy == FG_SPLIT_PER_1K) {
-      for (int s = 0; s < S; ++s)
-        seq_splits[size_t(s)] = std::min<int64_t>(std::max<int64_t>(1, seqs[s].kv_len / 1024), 16);
+      for (int s = 0; s < S; ++s) seq_splits[size_t(s)] = std::clamp<int64_t>(seqs[s].kv_len / 1024, 1, 16);
     }
 
     // ---- split each group's visible range [0, vis_end)

@@ -476,15 +476,15 @@ def _read_golden(name):
     return rows
 
 
-def test_figure_rule_matches_printed_example():
+def test_figure_counts_match_printed_example():
     rows = [tuple(map(int, r.split())) for r in _read_golden("figure_split_counts.txt")]
     lengths = [r[0] for r in rows]
-    assert split_policy.figure_rule(lengths) == [r[1] for r in rows]
+    assert split_policy.figure_counts(lengths) == [r[1] for r in rows]
 
 
-def test_host_heuristic_hand_derived_cases():
-    for row in _read_golden("host_heuristic_cases.txt"):
+def test_engine_counts_hand_derived_cases():
+    for row in _read_golden("engine_split_cases.txt"):
         head, lens, want = (part.split() for part in row.split("|"))
         sms, chunk = int(head[0]), int(head[1])
-        got = split_policy.host_heuristic([int(x) for x in lens], sms, chunk)
+        got = split_policy.engine_counts([int(x) for x in lens], sms, chunk)
         assert got == [int(x) for x in want]

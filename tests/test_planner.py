@@ -190,7 +190,7 @@ def test_unused_table_entries_are_ignored():
 
 # ---- the pages' split policies, native in the planner, against the oracle's
 # restatements (which the golden files pin)
-from oracle.split_policy import figure_rule, host_heuristic  # noqa: E402
+from oracle.split_policy import engine_counts, figure_counts  # noqa: E402
 
 
 def _aligned(k, length):
@@ -223,10 +223,10 @@ def test_page_policies_match_oracle(policy, cus):
         spec = wl.custom_spec("p", [1] * n, ctx, 4, 4, 64, 64, seed=trial)
         lens = [c + 1 for c in ctx]
         if policy == "engine":
-            want = host_heuristic(lens, num_sms=cus, min_chunk_size=256)
+            want = engine_counts(lens, num_sms=cus, min_chunk_size=256)
             plan = plan_of(spec, target_cus=cus, split_policy=fgb.FG_SPLIT_ENGINE, max_splits=256)
         else:
-            want = figure_rule(lens)
+            want = figure_counts(lens)
             plan = plan_of(spec, target_cus=cus, split_policy=fgb.FG_SPLIT_PER_1K, max_splits=256)
         got = _splits_per_seq(plan, n)
         assert got == [_aligned(min(k, 256), L) for k, L in zip(want, lens)], (lens, want, got)
