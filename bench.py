@@ -173,9 +173,16 @@ def load_traffic(workload):
     return rec.get("attn_hbm_bytes_per_launch")
 
 
-def cpu_baseline(spec, tens, budget_s=30.0, min_s=10.0):
-    """The float64 oracle as it stands, timed on this host (append + attention)."""
-    from threadpoolctl import threadpool_info
+def cpu_baseline(spec, tens, budget_s=30.0, min_s=10.0, single_thread=False):
+    """The float64 oracle as it stands, timed on this host (append + attention).
+    With single_thread, BLAS is limited to one thread (and the result says so)."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    if single_thread:
+        with threadpool_limits(limits=1, user_api="blas"):
+            res = cpu_baseline(spec, tens, budget_s, min_s)
+        res["cores"] = 1
+        res["sample"] += "; BLAS limited to one thread"
+        return res
 
     from oracle import attention as ora
     from ragged_paged_attention_splitfuse_amd import workloads as wl
@@ -264,33 +271,48 @@ def trace_cpu_baseline(passes, hq, hkv, d, bs, seed, wl, n_sample=8):
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
-def run_trace(args, torch, fgb, wl):
-    """Replay the 512-request trace through the host SplitFuse scheduler.
+def replay_trace(torch, fgb, wl, reqs, clients, policy, warmup=1, trace_passes=0, separate=False,
+                 record_kernels=True):
+    """Replay a request trace through the host scheduler at `clients` closed-loop
+    clients under composition `policy`.
 
-    Every pass runs fg_plan_pass -> upload -> fg_kv_append ->
-    fg_attention_ragged on one pool.  Inputs of all passes come from the keyed
-    hash generator and are placed in HBM before timing starts.
-    """
+    Every pass runs fg_plan_pass -> upload + append -> fg_attention_ragged on
+    one pool.  Inputs of all passes come from the keyed hash generator and are
+    placed in HBM before timing starts.  Returns the passes, per-pass device
+    µs (HIP events on the launch stream, passes back to back), wall time, host
+    planning times and the library's per-kernel totals."""
     from ragged_paged_attention_splitfuse_amd import splitfuse as sf
 
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     hq = hkv = 32
     d, bs, seed = 128, 64, 5
-    reqs = sf.trace_requests()
     arrivals = {}
-    passes, nb = sf.schedule(reqs, clients=32, budget=2048, block_size=bs, seed=seed,
-                             policy=args.serve_policy, arrivals=arrivals)
+    passes, nb = sf.schedule(reqs, clients=clients, budget=2048, block_size=bs, seed=seed,
+                             policy=policy, arrivals=arrivals)
+    full_passes = len(passes)
+    if trace_passes > 0:
+        # a slice of the replay (the first N passes, e.g. for a profiled run)
+        passes = passes[:trace_passes]
     t_max = max(p.num_tokens for p in passes)
     kshape, vshape = fgb.pool_shapes(nb, hkv, bs, d)
     kp = torch.zeros(kshape, dtype=torch.bfloat16, device=dev)
     vp = torch.zeros(vshape, dtype=torch.bfloat16, device=dev)
-    inputs = []
+    # every pass's rows, generated in a few large slices and viewed per pass
+    rid_rows = np.concatenate([np.repeat(p.rids, p.q_lens) for p in passes])
+    pos_rows = np.concatenate([np.arange(c, c + n) for p in passes for c, n in zip(p.ctx_lens, p.q_lens)])
+    big = {}
+    for kind, h in ((wl.KIND_Q, hq), (wl.KIND_K, hkv), (wl.KIND_V, hkv)):
+        buf = torch.empty((len(rid_rows), h, d), dtype=torch.bfloat16, device=dev)
+        for a in range(0, len(rid_rows), 16384):
+            buf[a:a + 16384] = wl.hash_normal_bf16_torch(seed, kind, rid_rows[a:a + 16384],
+                                                         pos_rows[a:a + 16384], h, d, dev)
+        big[kind] = buf
+    inputs, r0 = [], 0
     for p in passes:
-        rid_rows = np.repeat(p.rids, p.q_lens)
-        pos_rows = np.concatenate([np.arange(c, c + n) for c, n in zip(p.ctx_lens, p.q_lens)])
-        inputs.append(tuple(wl.hash_normal_bf16_torch(seed, kind, rid_rows, pos_rows, h, d, dev)
-                            for kind, h in ((wl.KIND_Q, hq), (wl.KIND_K, hkv), (wl.KIND_V, hkv))))
+        r1 = r0 + p.num_tokens
+        inputs.append(tuple(big[kind][r0:r1] for kind in (wl.KIND_Q, wl.KIND_K, wl.KIND_V)))
+        r0 = r1
     max_meta = max_ws = 16
     for p in passes:
         pl = fgb.Plan(p.q_lens, p.ctx_lens, p.block_tables, hq, hkv, d, bs, nb)
@@ -302,8 +324,6 @@ def run_trace(args, torch, fgb, wl):
     out = torch.empty((t_max, hq, d), dtype=torch.float32, device=dev)
     lse = torch.empty((t_max, hq), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
-
-    separate = args.separate_append
 
     def replay(record):
         keep, evs, host = [], [], []
@@ -327,11 +347,12 @@ def run_trace(args, torch, fgb, wl):
             keep.append(plan)
         return keep, evs, host
 
-    for _ in range(max(0, args.warmup)):
+    for _ in range(max(0, warmup)):
         replay(False)
         torch.cuda.synchronize()
     fgb.fg_profile_read()
-    fgb.fg_profile_enable(True)
+    if record_kernels:
+        fgb.fg_profile_enable(True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     keep, evs, host = replay(True)
@@ -340,7 +361,34 @@ def run_trace(args, torch, fgb, wl):
     fgb.fg_profile_enable(False)
     kern = fgb.fg_profile_read()
     per = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
-    serving = sf.serving_metrics(reqs, sf.composition_of(passes), arrivals, per)
+    keep.clear()
+    del inputs, big, kp, vp
+    torch.cuda.empty_cache()
+    return {"passes": passes, "full_passes": full_passes, "arrivals": arrivals, "pool_blocks": nb,
+            "per_us": per, "wall_s": wall, "host_s": host, "kern": kern, "t_max": t_max,
+            "shape": (hq, hkv, d, bs, seed)}
+
+
+def full_budget_ref_us(passes, per_us, budget=2048):
+    """Median device time of the replay's passes that hold exactly `budget` tokens."""
+    full = [u for p, u in zip(passes, per_us) if p.num_tokens == budget]
+    return float(np.median(full)) if full else None
+
+
+def run_trace(args, torch, fgb, wl):
+    """Replay the 512-request trace through the host SplitFuse scheduler."""
+    from ragged_paged_attention_splitfuse_amd import splitfuse as sf
+
+    reqs = sf.trace_requests()
+    r = replay_trace(torch, fgb, wl, reqs, args.clients, args.serve_policy, warmup=args.warmup,
+                     trace_passes=args.trace_passes, separate=args.separate_append)
+    passes, per, wall, kern = r["passes"], r["per_us"], r["wall_s"], r["kern"]
+    hq, hkv, d, bs, seed = r["shape"]
+    serving = None
+    if len(passes) == r["full_passes"]:
+        t_ref = full_budget_ref_us(passes, per)
+        sla = sf.sla_of(t_ref, 2048, args.sla_ttft_factor, args.sla_tpot_factor) if t_ref else None
+        serving = sf.serving_metrics(reqs, sf.composition_of(passes), r["arrivals"], per, sla=sla)
     toks = sum(p.num_tokens for p in passes)
     kv_bytes = sum(int(np.sum(p.q_lens.astype(np.int64) + p.ctx_lens)) * hkv * d * 4 for p in passes)
     flops = sum(4 * d * hq * int(np.sum(p.q_lens.astype(np.int64) * p.ctx_lens
@@ -353,17 +401,17 @@ def run_trace(args, torch, fgb, wl):
         "ms_per_step": round(wall * 1e3 / len(passes), 5), "higher_is_better": False,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "trace512", "policy": args.serve_policy, "requests": len(reqs),
-                   "clients": 32, "budget": 2048, "max_pass_tokens": t_max,
+                   "clients": args.clients, "budget": 2048, "max_pass_tokens": r["t_max"],
                    "q_heads": hq, "kv_heads": hkv, "head_dim": d, "block_size": bs,
-                   "passes": len(passes), "pool_blocks": nb},
+                   "passes": len(passes), "trace_passes": r["full_passes"], "pool_blocks": r["pool_blocks"]},
         "roofline": None, "cpu_baseline": None,
         "detail": {
             "total_ms": round(wall * 1e3, 3), "tokens": toks,
             "tokens_per_s": round(toks / wall, 1),
             "pass_device_us": {q: round(float(np.percentile(per, v)), 2)
-                               for q, v in (("p50", 50), ("p90", 90), ("p99", 99), ("max", 100))},
+                               for q, v in (("p10", 10), ("p50", 50), ("p90", 90), ("p99", 99), ("max", 100))},
             "device_total_ms": round(float(per.sum()) / 1e3, 3),
-            "host_plan_us_median": round(float(np.median(host)) * 1e6, 1),
+            "host_plan_us_median": round(float(np.median(r["host_s"])) * 1e6, 1),
             "kernel_ms_total": {k: round(v[0], 3) for k, v in kern.items()},
             "attn_gbs_avg": round(kv_bytes / (attn_ms * 1e-3) / 1e9, 1) if attn_ms else None,
             "attn_tflops_avg": round(flops / (attn_ms * 1e-3) / 1e12, 2) if attn_ms else None,
@@ -371,10 +419,56 @@ def run_trace(args, torch, fgb, wl):
             "serving_on_device_timeline": serving,
         },
     }
-    keep.clear()
     if not args.no_cpu:
         res["cpu_baseline"] = trace_cpu_baseline(passes, hq, hkv, d, bs, seed, wl)
         res["detail"]["gpu_vs_oracle"] = round(res["cpu_baseline"]["value"] / res["value"], 1)
+    print(json.dumps(res), flush=True)
+
+
+SERVE_CLIENTS = (1, 2, 4, 8, 16, 32)
+
+
+def run_serve_sweep(args, torch, fgb, wl):
+    """The 512-request trace at 1 .. 32 closed-loop clients under each pass
+    composition (the benchmark setup of the research summary, "Key points"),
+    with the user-facing metrics and the effective throughput on the device
+    timeline.  The SLA unit t_ref is the median full-budget SplitFuse pass of
+    the 32-client replay, shared by every point of the sweep."""
+    from ragged_paged_attention_splitfuse_amd import splitfuse as sf
+
+    reqs = sf.trace_requests()
+    runs = {}
+    order = [(c, pol) for c in sorted(SERVE_CLIENTS, reverse=True) for pol in sf.POLICIES]
+    for i, (clients, pol) in enumerate(order):
+        r = replay_trace(torch, fgb, wl, reqs, clients, pol, warmup=1 if i == 0 else 0,
+                         separate=args.separate_append, record_kernels=False)
+        runs[(clients, pol)] = r
+        print(json.dumps({"clients": clients, "policy": pol, "passes": len(r["passes"]),
+                          "device_ms": round(float(r["per_us"].sum()) / 1e3, 2)}), file=sys.stderr, flush=True)
+    top = runs[(max(SERVE_CLIENTS), "splitfuse")]
+    t_ref = full_budget_ref_us(top["passes"], top["per_us"])
+    sla = sf.sla_of(t_ref, 2048, args.sla_ttft_factor, args.sla_tpot_factor)
+    points = []
+    for (clients, pol), r in sorted(runs.items()):
+        m = sf.serving_metrics(reqs, sf.composition_of(r["passes"]), r["arrivals"], r["per_us"], sla=sla)
+        points.append({"clients": clients, "policy": pol, "passes": m["passes"],
+                       "requests_per_s": m["requests_per_s"],
+                       "effective_requests_per_s": m["effective_requests_per_s"], "sla_met": m["sla_met"],
+                       "ttft_us_p50": m["ttft_us"]["p50"], "ttft_us_p99": m["ttft_us"]["p99"],
+                       "tpot_us_p50": m["tpot_us"]["p50"], "tpot_us_p99": m["tpot_us"]["p99"],
+                       "token_gap_us_p99": m["token_gap_us"]["p99"], "token_gap_us_max": m["token_gap_us"]["max"],
+                       "host_plan_us_median": round(float(np.median(r["host_s"])) * 1e6, 1)})
+    best = max(p["effective_requests_per_s"] for p in points if p["policy"] == "splitfuse")
+    res = {"metric": "effective throughput of the attention layer over 1-32 clients (requests/s meeting "
+                     "the attention-level SLA, device timeline), 7B shape",
+           "value": best, "unit": "requests/s (SplitFuse, best client count)", "n_gpus": 1,
+           "steps": sum(len(r["passes"]) for r in runs.values()), "warmup": 1,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic", "config": {"workload": "serve_sweep", "requests": len(reqs),
+                                           "clients": list(SERVE_CLIENTS), "policies": list(sf.POLICIES),
+                                           "budget": 2048},
+           "roofline": None, "cpu_baseline": None,
+           "detail": {"sla": sla, "points": points}}
     print(json.dumps(res), flush=True)
 
 
@@ -556,6 +650,14 @@ def main():
                     help="upload the plan and append K/V in two launches instead of one")
     ap.add_argument("--serve-policy", choices=["splitfuse", "orca", "prefill_first"],
                     default="splitfuse", help="pass composition of the trace512 replay")
+    ap.add_argument("--clients", type=int, default=32,
+                    help="trace512: closed-loop clients (the pages' benchmark uses 1-32)")
+    ap.add_argument("--sla-ttft-factor", type=float, default=3.0,
+                    help="SLA: TTFT <= factor x t_ref x ceil(prompt / budget)")
+    ap.add_argument("--sla-tpot-factor", type=float, default=1.5,
+                    help="SLA: TPOT <= factor x t_ref (t_ref: median full-budget pass)")
+    ap.add_argument("--trace-passes", type=int, default=0,
+                    help="trace512: replay only the first N passes (0 = all; for profiled runs)")
     ap.add_argument("--no-achievable", action="store_true",
                     help="skip the achievable-peak probes (copy, read stream and bf16 GEMM)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -590,6 +692,9 @@ def main():
     if args.workload == "trace512":
         run_trace(args, torch, fgb, wl)
         return
+    if args.workload == "serve_sweep":
+        run_serve_sweep(args, torch, fgb, wl)
+        return
     if args.workload == "sweep":
         run_sweep(args, torch, fgb, wl, dev, stream, knobs_of(args, fgb))
         return
@@ -602,6 +707,20 @@ def main():
                      args.separate_append, args.kernel_events)
     step, keep, kern, info = m["step"], m["keep"], m["kern"], m["info"]
     host_plan_s, ms_per_step = m["host_plan_s"], m["ms_per_step"]
+
+    # warm passes one by one: each bracketed by HIP events on the launch stream,
+    # back to back, for the per-pass distribution (median, p10, p90)
+    warm = []
+    evs = []
+    for _ in range(args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step(keep)
+        e1.record(stream)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    warm = [a.elapsed_time(b) * 1e3 for a, b in evs]
+    keep.clear()
 
     # cold-cache passes: 1 GiB written between passes evicts L2 and the 256 MB MALL
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -678,6 +797,10 @@ def main():
             "pass_roofline_frac": round(max(hbm_floor_us, mfma_floor_us) / pass_us, 4),
             "append_gbs": round(alg["append_bytes"] / (app_us * 1e-6) / 1e9, 1),
             "host_plan_us_median": round(float(np.median(host_plan_s)) * 1e6, 1) if host_plan_s else None,
+            "warm_pass_device_us": {"p10": round(float(np.percentile(warm, 10)), 2),
+                                    "median": round(float(np.median(warm)), 2),
+                                    "p90": round(float(np.percentile(warm, 90)), 2),
+                                    "passes": len(warm)} if warm else None,
             "cold_pass_us": {"p10": round(float(np.percentile(cold, 10)), 2),
                              "median": round(float(np.median(cold)), 2),
                              "p90": round(float(np.percentile(cold, 90)), 2)} if cold else None,
@@ -705,6 +828,8 @@ def main():
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(spec, tens)
         res["detail"]["gpu_vs_oracle"] = round(res["cpu_baseline"]["value"] / pass_us, 1)
+        if spec.name == "tiny":
+            res["detail"]["cpu_baseline_single_thread"] = cpu_baseline(spec, tens, single_thread=True)
     print(json.dumps(res), flush=True)
 
 

@@ -163,7 +163,22 @@ def compose(requests, clients=32, budget=2048, policy="splitfuse", arrivals=None
     return passes
 
 
-def serving_metrics(requests, comp, arrivals, pass_us):
+def sla_of(t_ref_us, budget, ttft_factor=3.0, tpot_factor=1.5):
+    """Attention-level service levels, in units of one full-budget pass.
+
+    The pages judge serving by requests that complete within deadlines on the
+    time to first token and on the pace of streamed tokens (research summary,
+    idea I4 "effective throughput"; FastGen Guide, the goodput table and its
+    per-token deadline), with whole-model values in milliseconds.  Here only
+    the attention layer runs, so the deadlines are stated in units of t_ref,
+    the device time of one full-budget pass of the same shape: a request
+    meets them when its TTFT <= ttft_factor * t_ref * ceil(prompt / budget)
+    and its TPOT <= tpot_factor * t_ref."""
+    return {"t_ref_us": float(t_ref_us), "budget": int(budget), "ttft_factor": float(ttft_factor),
+            "tpot_factor": float(tpot_factor)}
+
+
+def serving_metrics(requests, comp, arrivals, pass_us, sla=None):
     """User-facing metrics of a composed trace on a measured timeline.
 
     comp: compose() output; arrivals: its rid -> first-joinable pass index;
@@ -175,7 +190,9 @@ def serving_metrics(requests, comp, arrivals, pass_us):
     the tail; latency = last-token time - arrival time.  Time to first token
     and a steady token pace are the user-facing measures the research summary
     names (idea I4); the pages' absolute SLA figures belong to whole-model
-    passes and are not used here.
+    passes and are not used here.  With `sla` (see sla_of), effective
+    throughput counts only the requests that meet both deadlines: requests
+    meeting them per second of the whole replay.
     """
     ends = np.cumsum(np.asarray(pass_us, dtype=np.float64))
     prompt_len = {r.rid: r.prompt for r in requests}
@@ -194,12 +211,20 @@ def serving_metrics(requests, comp, arrivals, pass_us):
                 first[rid] = last[rid] = ends[i]
                 ntok[rid] = 1
     ttft, tpot, lat = [], [], []
+    met = 0
     for r in requests:
         a = start(arrivals[r.rid])
         ttft.append(first[r.rid] - a)
         lat.append(last[r.rid] - a)
+        pace = None
         if ntok[r.rid] > 1:
-            tpot.append((last[r.rid] - first[r.rid]) / (ntok[r.rid] - 1))
+            pace = (last[r.rid] - first[r.rid]) / (ntok[r.rid] - 1)
+            tpot.append(pace)
+        if sla is not None:
+            chunks = -(-r.prompt // sla["budget"])
+            ok = ttft[-1] <= sla["ttft_factor"] * sla["t_ref_us"] * chunks
+            ok = ok and (pace is None or pace <= sla["tpot_factor"] * sla["t_ref_us"])
+            met += int(ok)
 
     def pct(x):
         x = np.asarray(x, dtype=np.float64)
@@ -209,11 +234,16 @@ def serving_metrics(requests, comp, arrivals, pass_us):
 
     total = float(ends[-1]) if len(ends) else 0.0
     out_tokens = sum(r.output for r in requests)
-    return {"ttft_us": pct(ttft), "tpot_us": pct(tpot), "token_gap_us": pct(gaps),
-            "latency_us": pct(lat), "total_us": round(total, 1),
-            "requests_per_s": round(len(requests) / (total * 1e-6), 2) if total else None,
-            "output_tokens_per_s": round(out_tokens / (total * 1e-6), 1) if total else None,
-            "passes": len(comp)}
+    res = {"ttft_us": pct(ttft), "tpot_us": pct(tpot) if tpot else None, "token_gap_us": pct(gaps) if gaps else None,
+           "latency_us": pct(lat), "total_us": round(total, 1),
+           "requests_per_s": round(len(requests) / (total * 1e-6), 2) if total else None,
+           "output_tokens_per_s": round(out_tokens / (total * 1e-6), 1) if total else None,
+           "passes": len(comp)}
+    if sla is not None:
+        res["sla"] = dict(sla)
+        res["sla_met"] = met
+        res["effective_requests_per_s"] = round(met / (total * 1e-6), 2) if total else None
+    return res
 
 
 def schedule(requests, clients=32, budget=2048, block_size=64, seed=5, slack=1.25,

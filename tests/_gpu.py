@@ -101,6 +101,24 @@ def subset(spec, tens, seqs):
     return sub, st, rows
 
 
+def band_subpass(spec, tens, s, j0, j1):
+    """Rows j0..j1-1 of sequence s as a pass of their own: a chunk of j1 - j0
+    tokens at context ctx_s + j0, whose history is the sequence's logical K/V
+    before it.  Causal attention of a row depends only on its position and the
+    keys before it, so the sub-pass's rows equal those rows of the full pass.
+    Returns (sub_spec, sub_tensors, row_index into the full pass)."""
+    from tests._passes import logical_kv
+    c = int(spec.ctx_lens[s])
+    k_all, v_all = logical_kv(spec, tens)[s]
+    cu = np.zeros(spec.num_seqs + 1, np.int64)
+    cu[1:] = np.cumsum(spec.q_lens)
+    sub = wl.custom_spec(spec.name + "-band", [j1 - j0], [c + j0], spec.num_q_heads,
+                         spec.num_kv_heads, spec.head_dim, spec.block_size, seed=1, slack=1.0)
+    st = wl.PassTensors(q=tens.q[cu[s] + j0:cu[s] + j1], k_new=k_all[c + j0:c + j1],
+                        v_new=v_all[c + j0:c + j1], hist_k=k_all[:c + j0], hist_v=v_all[:c + j0])
+    return sub, st, np.arange(cu[s] + j0, cu[s] + j1)
+
+
 def oracle_pass(spec, tens):
     kp, vp = oracle_pools(spec, tens, poison=True)
     return ora.attend(tens.q, kp, vp, spec.q_lens, spec.ctx_lens, spec.block_tables,
@@ -117,6 +135,30 @@ def trace_pass_inputs(p, seed, hq, hkv, d, device="cuda"):
     return q.contiguous(), k.contiguous(), v.contiguous()
 
 
+def _trace_seq_bits(p, seqs, seed, num_heads, head_dim):
+    """Q (this pass's rows) and whole-history K, V bits of sequences `seqs` of
+    a scheduled pass, heads 0..num_heads-1, from the keyed generator on the
+    CPU (torch's vectorised version; same bits as the numpy one)."""
+    ctx = p.ctx_lens[seqs].astype(np.int64)
+    n = p.q_lens[seqs].astype(np.int64)
+    rids = p.rids[seqs].astype(np.int64)
+    q_pos = np.concatenate([np.arange(c, c + m) for c, m in zip(ctx, n)])
+    kv_pos = np.concatenate([np.arange(0, c + m) for c, m in zip(ctx, n)])
+    def gen(kind, rid_rows, pos):
+        # 64-token slices keep the int64 temporaries cache-resident
+        out = np.empty((len(pos), num_heads, head_dim), np.uint16)
+        for a in range(0, len(pos), 64):
+            t = wl.hash_normal_bf16_torch(seed, kind, rid_rows[a:a + 64], pos[a:a + 64], num_heads,
+                                          head_dim, "cpu")
+            out[a:a + 64] = t.view(torch.int16).numpy().view(np.uint16)
+        return out
+
+    q = gen(wl.KIND_Q, np.repeat(rids, n), q_pos)
+    k = gen(wl.KIND_K, np.repeat(rids, ctx + n), kv_pos)
+    v = gen(wl.KIND_V, np.repeat(rids, ctx + n), kv_pos)
+    return q, k, v
+
+
 def trace_oracle(p, seqs, heads, seed, head_dim, block_size):
     """Oracle rows for sequences `seqs` of a scheduled pass, on q/kv heads `heads`.
 
@@ -125,18 +167,20 @@ def trace_oracle(p, seqs, heads, seed, head_dim, block_size):
     The sub-pass is MHA over the chosen heads with compact block ids.
     """
     hs = list(heads)
+    seqs = list(seqs)
     q_lens = p.q_lens[seqs].astype(np.int32)
     ctx = p.ctx_lens[seqs].astype(np.int32)
-    qs, kn, vn, hk, hv = [], [], [], [], []
-    for s in seqs:
-        rid, c, n = int(p.rids[s]), int(p.ctx_lens[s]), int(p.q_lens[s])
-        qs.append(wl.hash_normal_bf16(seed, wl.KIND_Q, rid, np.arange(c, c + n), hs, head_dim))
-        k = wl.hash_normal_bf16(seed, wl.KIND_K, rid, np.arange(0, c + n), hs, head_dim)
-        v = wl.hash_normal_bf16(seed, wl.KIND_V, rid, np.arange(0, c + n), hs, head_dim)
-        hk.append(k[:c]); kn.append(k[c:]); hv.append(v[:c]); vn.append(v[c:])
+    qa, ka, va = _trace_seq_bits(p, seqs, seed, max(hs) + 1, head_dim)
+    qa, ka, va = qa[:, hs], ka[:, hs], va[:, hs]
+    hk, kn, hv, vn = [], [], [], []
+    o = 0
+    for c, n in zip(ctx, q_lens):
+        hk.append(ka[o:o + c]); kn.append(ka[o + c:o + c + n])
+        hv.append(va[o:o + c]); vn.append(va[o + c:o + c + n])
+        o += c + n
     spec = wl.custom_spec("trace-sub", q_lens, ctx, len(hs), len(hs), head_dim, block_size,
                           seed=1, slack=1.0)
-    tens = wl.PassTensors(q=np.concatenate(qs), k_new=np.concatenate(kn), v_new=np.concatenate(vn),
+    tens = wl.PassTensors(q=np.ascontiguousarray(qa), k_new=np.concatenate(kn), v_new=np.concatenate(vn),
                           hist_k=np.concatenate(hk), hist_v=np.concatenate(hv))
     return oracle_pass(spec, tens)
 

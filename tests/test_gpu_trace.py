@@ -1,6 +1,7 @@
 """Trace replay on the GPU: Dynamic SplitFuse passes from the host scheduler,
 every pass through fg_plan_pass -> upload -> fg_kv_append ->
-fg_attention_ragged on one pool, sampled passes checked against the oracle.
+fg_attention_ragged on one pool; every row (all sequences, all heads) of the
+kept passes checked against the oracle.
 """
 import numpy as np
 import pytest
@@ -36,32 +37,34 @@ def _replay(passes, nb, hq, hkv, d, bs, seed, keep):
 
 def _check_pass(p, got, seqs, heads, seed, d, bs, g=1):
     out, lse = got
+    heads = list(heads)
     o_ref, l_ref = G.trace_oracle(p, seqs, heads, seed, d, bs)
     cu = np.zeros(len(p.q_lens) + 1, np.int64)
     cu[1:] = np.cumsum(p.q_lens)
     rows = np.concatenate([np.arange(cu[s], cu[s + 1]) for s in seqs])
     o = out[rows][:, heads]
     l_ = lse[rows][:, heads]
-    compare(o, l_, o_ref, l_ref, f"trace pass {p.index} seqs {len(seqs)} heads {list(heads)}")
+    compare(o, l_, o_ref, l_ref, f"trace pass {p.index}: {len(seqs)} seqs x {len(heads)} heads")
 
 
-def test_small_gqa_trace_all_rows():
+@pytest.mark.parametrize("clients", [1, 8])
+def test_small_gqa_trace_all_rows(clients):
     reqs = sf.trace_requests(48, seed=11, prompt_mean=600, prompt_sd=180, out_mean=10, out_sd=3)
-    passes, nb = sf.schedule(reqs, clients=8, budget=512, block_size=16, seed=11)
+    passes, nb = sf.schedule(reqs, clients=clients, budget=512, block_size=16, seed=11)
     keep = [3, len(passes) // 2, len(passes) - 2]
-    _log(f"[case] small trace passes={len(passes)} nb={nb} keep={keep}")
+    _log(f"[case] small trace clients={clients} passes={len(passes)} nb={nb} keep={keep}")
     got = _replay(passes, nb, 8, 2, 64, 16, 11, keep)
     for i in keep:
         p = passes[i]
-        # GQA 8:2 -- the oracle sub-pass is MHA per head, so check kv head 1's
-        # q heads against that kv head's regenerated K/V
+        # GQA 8:2 -- the oracle sub-pass is MHA per head, so check every q
+        # head against its kv head's regenerated K/V
         out, lse = got[i]
-        for qh in (4, 7):
-            o_ref, l_ref = G.trace_oracle_gqa(p, list(range(len(p.q_lens))), qh, 1, 11, 64, 16)
+        for qh in range(8):
+            o_ref, l_ref = G.trace_oracle_gqa(p, list(range(len(p.q_lens))), qh, qh // 4, 11, 64, 16)
             compare(out[:, [qh]], lse[:, [qh]], o_ref, l_ref, f"small trace pass {i} q head {qh}")
 
 
-def test_full_trace_sampled_passes():
+def test_full_trace_kept_passes_every_row():
     reqs = sf.trace_requests()
     passes, nb = sf.schedule(reqs)
     most = max(range(len(passes)), key=lambda i: (len(passes[i].q_lens), i))
@@ -74,9 +77,7 @@ def test_full_trace_sampled_passes():
     got = _replay(passes, nb, 32, 32, 128, 64, 5, keep)
     for i in keep:
         p = passes[i]
-        chunks = list(range(p.num_decodes, len(p.q_lens)))
-        seqs = sorted(set(chunks[:3] + list(range(min(3, p.num_decodes)))))
-        _check_pass(p, got[i], seqs, [0, 21], 5, 128, 64)
+        _check_pass(p, got[i], list(range(len(p.q_lens))), range(32), 5, 128, 64)
 
 
 @pytest.mark.parametrize("policy", ["orca", "prefill_first"])
@@ -92,5 +93,4 @@ def test_baseline_composition_oversized_passes(policy):
     got = _replay(passes, nb, 32, 32, 128, 64, 7, keep)
     for i in keep:
         p = passes[i]
-        seqs = list(range(min(4, len(p.q_lens))))
-        _check_pass(p, got[i], seqs, [3], 7, 128, 64)
+        _check_pass(p, got[i], list(range(len(p.q_lens))), range(32), 7, 128, 64)

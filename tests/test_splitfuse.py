@@ -165,3 +165,21 @@ def test_serving_metrics_on_a_hand_timeline():
     assert m["tpot_us"]["mean"] == 35
     assert sorted([m["token_gap_us"]["max"], m["token_gap_us"]["p50"]]) == [35, 40]
     assert m["latency_us"]["max"] == 100 and m["total_us"] == 150
+
+
+def test_effective_throughput_counts_requests_within_both_deadlines():
+    # the hand timeline above: r0 TTFT 30 (prompt 3 = 2 chunks of budget 2),
+    # TPOT 35; r1 TTFT 50 (1 chunk), a single token (no pace to judge)
+    reqs = [sf.TraceRequest(0, 3, 3), sf.TraceRequest(1, 2, 1)]
+    arr = {}
+    comp = sf.compose(reqs, clients=1, budget=2, policy="splitfuse", arrivals=arr)
+    pass_us = [10, 20, 30, 40, 50]
+    # t_ref 20: r0 needs TTFT <= f1*20*2 and TPOT <= f2*20; r1 TTFT <= f1*20
+    cases = [((3.0, 1.5), 1),    # r0: 30 <= 120 but 35 > 30; r1: 50 <= 60
+             ((3.0, 2.0), 2),    # r0: 35 <= 40; r1 as before
+             ((2.0, 2.0), 1),    # r1: 50 > 40
+             ((0.5, 5.0), 0)]    # r0: 30 > 20; r1: 50 > 10
+    for (f1, f2), want in cases:
+        m = sf.serving_metrics(reqs, comp, arr, pass_us, sla=sf.sla_of(20.0, 2, f1, f2))
+        assert m["sla_met"] == want, (f1, f2, m["sla_met"])
+        assert m["effective_requests_per_s"] == round(want / 150e-6, 2)
