@@ -230,6 +230,27 @@ fg_status fg_attention_ragged(const fg_plan* plan, void* d_meta,
                               void* out, int32_t out_dtype, float* lse,
                               void* d_ws, size_t ws_bytes, void* stream);
 
+/* fg_attention_ragged for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same kernels and results, bit for bit, with no workspace
+ * argument.  The split partial rows go to a library-owned scratch array that
+ * sits in the library's code object on each GPU (fg_noalloc_scratch_bytes()
+ * bytes, 32 MiB, held by every GPU the library runs on until the process
+ * ends).  The call allocates nothing, creates no events (fg_profile_enable
+ * does not bracket it) and needs no initialisation.  Arguments, layouts,
+ * ownership and errors as for fg_attention_ragged, plus FG_E_WORKSPACE when
+ * the plan's workspace_bytes exceed the scratch size, FG_E_HIP if the
+ * scratch's device address cannot be looked up, FG_E_UNSUPPORTED past 64
+ * devices.  Every call on one GPU shares that GPU's scratch (its contents on
+ * entry do not matter): calls that overlap in time on one GPU, on any
+ * streams, race and give undefined results. */
+fg_status fg_attention_ragged_noalloc(const fg_plan* plan, void* d_meta,
+                                      const void* q, const void* k_pool, const void* v_pool,
+                                      void* out, int32_t out_dtype, float* lse, void* stream);
+
+/* Size in bytes of the scratch array behind fg_attention_ragged_noalloc. */
+size_t fg_noalloc_scratch_bytes(void);
+
 /* Free a plan (NULL is allowed).  Only after the stream has passed every
  * call that used it. */
 void fg_plan_destroy(fg_plan* plan);

@@ -79,6 +79,9 @@ SIGNATURES = {
     "fg_attention_ragged": (ctypes.c_int32, [ctypes.c_void_p] * 6 + [ctypes.c_int32, ctypes.c_void_p,
                                                                      ctypes.c_void_p, ctypes.c_size_t,
                                                                      ctypes.c_void_p]),
+    "fg_attention_ragged_noalloc": (ctypes.c_int32, [ctypes.c_void_p] * 6 + [ctypes.c_int32, ctypes.c_void_p,
+                                                                             ctypes.c_void_p]),
+    "fg_noalloc_scratch_bytes": (ctypes.c_size_t, []),
     "fg_plan_destroy": (None, [ctypes.c_void_p]),
     "fg_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
     "fg_abi_version": (ctypes.c_int32, []),
@@ -321,6 +324,30 @@ def fg_attention_ragged(plan, d_meta, q, k_pool, v_pool, out, lse=None, workspac
     return workspace
 
 
+def fg_attention_ragged_noalloc(plan, d_meta, q, k_pool, v_pool, out, lse=None, stream=None,
+                                out_dtype=None):
+    """fg_attention_ragged with the library's scratch array as its workspace
+    (nothing is allocated, here or in the library)."""
+    t, hq, hkv, d = plan.num_tokens, plan.num_q_heads, plan.num_kv_heads, plan.head_dim
+    kshape, vshape = pool_shapes(plan.num_blocks, hkv, plan.block_size, d)
+    if out_dtype is None:
+        import torch
+        out_dtype = FG_DTYPE_BF16 if (hasattr(out, "dtype") and out.dtype == torch.bfloat16) else FG_DTYPE_F32
+    _check_tensor(q, (t, hq, d), "bf16", "q")
+    _check_tensor(k_pool, kshape, "bf16", "k_pool")
+    _check_tensor(v_pool, vshape, "bf16", "v_pool")
+    _check_tensor(out, (t, hq, d), "bf16" if out_dtype == FG_DTYPE_BF16 else "f32", "out")
+    _check_tensor(lse, (t, hq), "f32", "lse")
+    _check(lib().fg_attention_ragged_noalloc(plan.handle, _ptr(d_meta if d_meta is not None else plan.meta),
+                                             _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(out), int(out_dtype),
+                                             _ptr(lse), _stream(stream)),
+           "fg_attention_ragged_noalloc")
+
+
+def fg_noalloc_scratch_bytes():
+    return int(lib().fg_noalloc_scratch_bytes())
+
+
 def fg_profile_enable(on=True, kernels=None):
     """Bracket launches with HIP events: every kernel, or only the FG_KERNEL_*
     ids in `kernels`; on=False turns it off."""
@@ -351,3 +378,4 @@ def fg_probe_read_stream(buf, sink, stream=None):
 kv_append = fg_kv_append
 upload_append = fg_upload_append
 attention_ragged = fg_attention_ragged
+attention_ragged_noalloc = fg_attention_ragged_noalloc

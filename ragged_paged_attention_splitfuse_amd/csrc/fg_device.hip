@@ -983,8 +983,9 @@ struct ProfScope {
   int kind;
   hipStream_t stream;
   hipEvent_t start = nullptr;
+  // kind FG_KERNEL_COUNT (or above): never bracketed, no event is created
   ProfScope(int k, hipStream_t s) : kind(k), stream(s) {
-    if (((g_prof_mask >> kind) & 1u) == 0) return;
+    if (kind < 0 || kind >= FG_KERNEL_COUNT || ((g_prof_mask >> kind) & 1u) == 0) return;
     std::lock_guard<std::mutex> lk(g_prof_mu);
     start = prof_event();
     if (start && hipEventRecord(start, stream) != hipSuccess) {
@@ -1166,20 +1167,15 @@ extern "C" fg_status fg_upload_append(const fg_plan* plan, void* d_meta, const v
   return fg_kv_append(plan, d_meta, k_new, v_new, k_pool, v_pool, stream);
 }
 
-extern "C" fg_status fg_attention_ragged(const fg_plan* plan, void* d_meta, const void* q,
-                                         const void* k_pool, const void* v_pool, void* out,
-                                         int32_t out_dtype, float* lse, void* d_ws,
-                                         size_t ws_bytes, void* stream) {
-  if (!plan) return FG_E_INVALID;
-  if (out_dtype != FG_DTYPE_F32 && out_dtype != FG_DTYPE_BF16) return FG_E_UNSUPPORTED;
-  if (plan->n_items == 0) return FG_OK;
-  if (!d_meta || !q || !k_pool || !v_pool || !out) return FG_E_INVALID;
-  if (!aligned16(d_meta) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) ||
-      !aligned16(out) || (lse && !aligned16(lse)))
-    return FG_E_INVALID;
-  if (plan->ws_bytes > 0 && (!d_ws || ws_bytes < plan->ws_bytes || !aligned16(d_ws)))
-    return FG_E_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+namespace fg {
+namespace {
+
+// The attention launch (and the merge launch when the plan splits prefill
+// tiles) with the workspace at d_ws, which must already be checked against
+// the plan.  `profile` allows the per-launch HIP events of fg_profile_enable.
+fg_status launch_attention(const fg_plan* plan, void* d_meta, const void* q, const void* k_pool,
+                           const void* v_pool, void* out, int32_t out_dtype, float* lse, void* d_ws,
+                           hipStream_t s, bool profile) {
   uint8_t* meta = static_cast<uint8_t*>(d_meta);
   AttnArgs a;
   a.seqs = reinterpret_cast<const SeqRec*>(meta + plan->off_seqs);
@@ -1203,7 +1199,7 @@ extern "C" fg_status fg_attention_ragged(const fg_plan* plan, void* d_meta, cons
   a.out_bf16 = out_dtype == FG_DTYPE_BF16;
 
   {
-    ProfScope prof(FG_KERNEL_ATTENTION, s);
+    ProfScope prof(profile ? FG_KERNEL_ATTENTION : FG_KERNEL_COUNT, s);
     const dim3 grid(unsigned(plan->n_items));
 #define FG_LAUNCH_ATTN(D_, B_)                                                                 \
   do {                                                                                         \
@@ -1218,7 +1214,7 @@ extern "C" fg_status fg_attention_ragged(const fg_plan* plan, void* d_meta, cons
   }
   const int32_t n_late = plan->n_merge_groups - plan->n_inlaunch_groups;
   if (n_late > 0) {
-    ProfScope prof(FG_KERNEL_MERGE, s);
+    ProfScope prof(profile ? FG_KERNEL_MERGE : FG_KERNEL_COUNT, s);
     if (plan->head_dim == 64)
       hipLaunchKernelGGL((merge_kernel<64>), dim3(unsigned(n_late)), dim3(kThreads), 0, s, a);
     else
@@ -1227,6 +1223,82 @@ extern "C" fg_status fg_attention_ragged(const fg_plan* plan, void* d_meta, cons
   }
   return FG_OK;
 }
+
+fg_status check_attention_args(const fg_plan* plan, int32_t out_dtype, const void* d_meta,
+                               const void* q, const void* k_pool, const void* v_pool,
+                               const void* out, const float* lse) {
+  if (out_dtype != FG_DTYPE_F32 && out_dtype != FG_DTYPE_BF16) return FG_E_UNSUPPORTED;
+  if (!d_meta || !q || !k_pool || !v_pool || !out) return FG_E_INVALID;
+  if (!aligned16(d_meta) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) ||
+      !aligned16(out) || (lse && !aligned16(lse)))
+    return FG_E_INVALID;
+  return FG_OK;
+}
+
+// ---------------------------------------------------------------- library scratch
+// Workspace of fg_attention_ragged_noalloc: one array per device in the code
+// object, allocated when the library is loaded onto the device and held until
+// the process ends.  In host code `scratch` names a host-side stand-in, not
+// device memory: its device address is looked up once per device with
+// hipGetSymbolAddress (that device current) and only that address is used.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+fg_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FG_E_HIP;
+  if (dev >= kMaxDevices) return FG_E_UNSUPPORTED;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return FG_E_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return FG_OK;
+}
+
+}  // namespace
+}  // namespace fg
+
+extern "C" fg_status fg_attention_ragged(const fg_plan* plan, void* d_meta, const void* q,
+                                         const void* k_pool, const void* v_pool, void* out,
+                                         int32_t out_dtype, float* lse, void* d_ws,
+                                         size_t ws_bytes, void* stream) {
+  if (!plan) return FG_E_INVALID;
+  if (out_dtype != FG_DTYPE_F32 && out_dtype != FG_DTYPE_BF16) return FG_E_UNSUPPORTED;
+  if (plan->n_items == 0) return FG_OK;
+  const fg_status st = check_attention_args(plan, out_dtype, d_meta, q, k_pool, v_pool, out, lse);
+  if (st != FG_OK) return st;
+  if (plan->ws_bytes > 0 && (!d_ws || ws_bytes < plan->ws_bytes || !aligned16(d_ws)))
+    return FG_E_WORKSPACE;
+  return launch_attention(plan, d_meta, q, k_pool, v_pool, out, out_dtype, lse, d_ws,
+                          static_cast<hipStream_t>(stream), true);
+}
+
+extern "C" fg_status fg_attention_ragged_noalloc(const fg_plan* plan, void* d_meta, const void* q,
+                                                 const void* k_pool, const void* v_pool, void* out,
+                                                 int32_t out_dtype, float* lse, void* stream) {
+  if (!plan) return FG_E_INVALID;
+  if (out_dtype != FG_DTYPE_F32 && out_dtype != FG_DTYPE_BF16) return FG_E_UNSUPPORTED;
+  if (plan->n_items == 0) return FG_OK;
+  fg_status st = check_attention_args(plan, out_dtype, d_meta, q, k_pool, v_pool, out, lse);
+  if (st != FG_OK) return st;
+  if (plan->ws_bytes > kScratchBytes) return FG_E_WORKSPACE;
+  void* ws = nullptr;
+  if (plan->ws_bytes > 0) {
+    st = scratch_of_current_device(&ws);
+    if (st != FG_OK) return st;
+  }
+  return launch_attention(plan, d_meta, q, k_pool, v_pool, out, out_dtype, lse, ws,
+                          static_cast<hipStream_t>(stream), false);
+}
+
+extern "C" size_t fg_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 extern "C" fg_status fg_profile_enable(int32_t mask) {
   std::lock_guard<std::mutex> lk(g_prof_mu);

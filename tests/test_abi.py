@@ -107,3 +107,20 @@ def test_missing_library_fails_loudly(tmp_path):
                          text=True, timeout=120)
     assert res.returncode == 0, res.stderr
     assert res.stdout.startswith("raised") and "not built" in res.stdout, res.stdout
+
+
+def test_noalloc_rejects_plans_past_its_scratch_before_any_device_call():
+    # A 7B 2048-token pass split 64 ways needs a workspace far past the scratch
+    # array: the call returns FG_E_WORKSPACE after the host-side checks, before
+    # any pointer is used (the addresses below are never dereferenced).
+    from ragged_paged_attention_splitfuse_amd import workloads as wl
+    spec = wl.config_spec(2)
+    plan = binding.Plan.from_spec(spec, force_splits=64, target_cus=256)
+    assert plan.info["workspace_bytes"] > binding.fg_noalloc_scratch_bytes() == 32 << 20
+    lib = binding.lib()
+    fake = 1 << 20
+    st = lib.fg_attention_ragged_noalloc(plan.handle, fake, fake, fake, fake, fake, 0, None, None)
+    assert st == binding.FG_E_WORKSPACE
+    assert lib.fg_attention_ragged_noalloc(None, fake, fake, fake, fake, fake, 0, None, None) == binding.FG_E_INVALID
+    assert lib.fg_attention_ragged_noalloc(plan.handle, fake, fake, fake, fake, fake, 7, None, None) == \
+        binding.FG_E_UNSUPPORTED
