@@ -811,6 +811,11 @@ __device__ void merge_group(const AttnArgs& a, const MergeRec& g, float* red) {
 // `last_flag` is the first word of the item's LDS (the merge uses the LDS
 // from 16 bytes on); the barrier before thread 0 writes it follows every LDS
 // access of the item.
+// The ordering argument above rests on gfx950's memory model (scoped sc1
+// accesses, stores counted by vmcnt): build the device code for gfx950 only.
+#if defined(__HIP_DEVICE_COMPILE__) && !defined(__gfx950__)
+#error "the in-launch split merge is written for gfx950's memory model"
+#endif
 template <int D>
 __device__ void finish_split(const AttnArgs& a, const ItemRec& it, int* last_flag) {
   __builtin_amdgcn_s_waitcnt(0);

@@ -269,6 +269,44 @@ def test_split_groups_merge_in_launch_and_rearm(name, splits):
     compare(runs[0][0], runs[0][1], o_ref, l_ref, f"in-launch merge {name}")
 
 
+@pytest.mark.parametrize("hq,hkv", [(16, 2), (8, 8)])   # one-wave GQA groups; vector-ALU rows
+def test_inlaunch_merge_stress_is_bit_stable(hq, hkv):
+    # Regression guard for the in-launch merge's ordering: a pass whose split
+    # decode and GQA groups all merge inside the attention launch, repeated 200
+    # times on one upload.  Every repetition must equal the first bit for bit
+    # (the merging work-group is whichever split finishes last, so a stale
+    # partial row would change the result); the run stops at the first
+    # mismatch.  The first result is also checked against the oracle.
+    spec = wl.custom_spec("stress", [1] * 24 + [2, 4], [int(x) for x in np.linspace(300, 6000, 24)] + [800, 2000],
+                          hq, hkv, 128, 64, seed=71)
+    _log(f"[case] in-launch merge stress hq={hq} hkv={hkv}, 200 launches")
+    tens = wl.make_tensors(spec)
+    kp, vp = G.gpu_pools(spec)
+    G.fill_history(spec, tens, kp, vp)
+    plan = fgb.Plan.from_spec(spec, force_splits=4, target_cus=256)
+    assert plan.info["num_inlaunch_merge_groups"] == plan.info["num_merge_groups"] > 0
+    meta = plan.upload()
+    q, kn, vn = G.to_dev(tens.q), G.to_dev(tens.k_new), G.to_dev(tens.v_new)
+    fgb.kv_append(plan, meta, kn, vn, kp, vp)
+    t, hq, d = spec.num_tokens, spec.num_q_heads, spec.head_dim
+    ws = torch.empty(max(16, plan.info["workspace_bytes"]), dtype=torch.uint8, device="cuda")
+    first = None
+    for i in range(200):
+        out = torch.empty((t, hq, d), dtype=torch.float32, device="cuda")
+        lse = torch.empty((t, hq), dtype=torch.float32, device="cuda")
+        fgb.attention_ragged(plan, meta, q, kp, vp, out, lse, workspace=ws)
+        if i % 20 == 19 or first is None:
+            torch.cuda.synchronize()
+        if first is None:
+            first = (out, lse)
+            continue
+        if i % 10 == 9:
+            torch.cuda.synchronize()
+        assert torch.equal(out, first[0]) and torch.equal(lse, first[1]), f"repetition {i} differs"
+    o_ref, l_ref = G.oracle_pass(spec, tens)
+    compare(first[0], first[1], o_ref, l_ref, f"in-launch merge stress hq={hq} hkv={hkv}")
+
+
 def plan_counter_offset(plan):
     lay = fgb.fg_plan_layout_t()
     fgb._check(fgb.lib().fg_plan_metadata(plan.handle, None, 0, ctypes.byref(lay)), "fg_plan_metadata")
