@@ -124,6 +124,29 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Block ids of a work item's KV range, held 64 at a time in one VGPR of each
+// wavefront (lane i holds table entry base + i), so that a step or stage picks
+// its block with a readlane instead of a dependent memory round trip before
+// its K/V loads.  `limit` is the number of used table entries of the sequence;
+// lanes past it hold 0 and are never selected.  base and the selected index
+// are wavefront-uniform.
+struct BlockWindow {
+  const int32_t* bt;
+  int limit;
+  int base;
+  int ids;
+  __device__ __forceinline__ void load(int first) {
+    base = first;
+    const int i = first + int(threadIdx.x & 63);
+    ids = i < limit ? bt[i] : 0;
+  }
+  // block id of table entry e (e >= base, uniform)
+  __device__ __forceinline__ int get(int e) {
+    if (e - base >= 64) load(e);
+    return __builtin_amdgcn_readlane(ids, e - base);
+  }
+};
+
 // Zero the bf16 elements of an 8-token chunk starting at `first` whose token
 // index is >= `valid` (slots past the end of a sequence may hold anything).
 __device__ __forceinline__ u32x4 zero_tail(u32x4 v, int first, int valid) {
@@ -194,11 +217,13 @@ __device__ void valu_item(const AttnArgs& a, const ItemRec& it, float* smem) {
   constexpr int HV = ST / kValuSubTile;     // 32-token V^T sub-blocks per step
   constexpr int UK = ST / TPI;              // K loads per step
   constexpr int UV = D / 16;                // V^T loads per half (16 dims each)
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const SeqRec sq = a.seqs[it.seq];
   const int32_t* bt = a.bt + sq.bt_off;
   const int G = a.group, g = it.kv_head;
   const int kv_valid = sq.kv_len;
+  BlockWindow win{bt, sq.nblk, 0, 0};
+  if constexpr (B >= ST) win.load((it.kv0 + wave * ST) / B);
   const int ktok = lane / LPT, kdc = lane % LPT;
   const int vd = lane >> 2, vtc = lane & 3;
 
@@ -228,7 +253,7 @@ __device__ void valu_item(const AttnArgs& a, const ItemRec& it, float* smem) {
   for (int t0 = it.kv0 + wave * ST; t0 < it.kv1; t0 += kWaves * ST) {
     u32x4 kr[UK], vr[HV][UV];
     int blk_u = 0;
-    if constexpr (B >= ST) blk_u = bt[t0 / B];
+    if constexpr (B >= ST) blk_u = win.get(t0 / B);
 #pragma unroll
     for (int i = 0; i < UK; ++i) {
       const int tok = t0 + i * TPI + ktok;
@@ -548,8 +573,10 @@ __device__ void mfma_item(const AttnArgs& a, const ItemRec& it, uint16_t* lds) {
       voff[i] = vt_off<D, B>(u / VU, 8 * min(u % VU, kKvTile / 8 - 1));
     }
   }
+  BlockWindow win{bt, sq.nblk, 0, 0};
+  if constexpr (B == kKvTile) win.load(it.kv0 / B);
   auto dma_stage = [&](int tb, int buf) {
-    const size_t tile = (size_t(bt[tb / B]) * a.hkv + kv_head_base) * (size_t(B) * D);
+    const size_t tile = (size_t(win.get(tb / B)) * a.hkv + kv_head_base) * (size_t(B) * D);
     uint16_t* kt = lds + buf * L::STAGE;
     uint16_t* vt = kt + L::KT;
 #pragma unroll
