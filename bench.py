@@ -479,7 +479,7 @@ def knobs_of(args, fgb):
 
 
 def measure_pass(torch, fgb, spec, tens, dev, stream, knobs, steps, warmup, separate=False,
-                 events="timed-attention"):
+                 events="timed-attention", api="pass"):
     """Set up pools and inputs of one pass, then time `steps` passes (plan,
     upload + append in one launch, attention; `separate` uses the two-launch
     upload and append) back to back after `warmup` untimed ones.
@@ -514,6 +514,10 @@ def measure_pass(torch, fgb, spec, tens, dev, stream, knobs, steps, warmup, sepa
         h0 = time.perf_counter()
         plan = fgb.Plan.from_spec(spec, **knobs)
         host_plan_s.append(time.perf_counter() - h0)
+        if api == "pass" and attention:
+            fgb.run_pass(plan, meta, q, kn, vn, kp, vp, out, lse, workspace=ws, stream=stream)
+            keep.append(plan)
+            return
         if separate:
             plan.upload(meta, stream)
             fgb.kv_append(plan, meta, kn, vn, kp, vp, stream)
@@ -588,7 +592,7 @@ def run_sweep(args, torch, fgb, wl, dev, stream, knobs):
         tens = wl.make_tensors(spec)
         alg = algorithmic(spec)
         m = measure_pass(torch, fgb, spec, tens, dev, stream, knobs, args.steps, args.warmup,
-                         args.separate_append, args.kernel_events)
+                         args.separate_append, args.kernel_events, args.api)
         ku = kernel_us(m["kern"])
         pass_us = m["ms_per_step"] * 1e3
         rows.append({"budget": budget, "pass_us": round(pass_us, 2),
@@ -646,6 +650,10 @@ def main():
                     help="where the per-launch HIP events go: around the attention launches "
                          "of the timed passes (default; upload+append timed in a second loop), "
                          "around every launch of the timed passes, or only in a second loop")
+    ap.add_argument("--api", choices=["pass", "append-then-attention"], default="pass",
+                    help="how a step runs: fg_pass (metadata upload, then one launch doing the KV "
+                         "append and the attention), or the plan upload + KV append launch "
+                         "followed by fg_attention_ragged")
     ap.add_argument("--separate-append", action="store_true",
                     help="upload the plan and append K/V in two launches instead of one")
     ap.add_argument("--serve-policy", choices=["splitfuse", "orca", "prefill_first"],
@@ -704,7 +712,7 @@ def main():
     t, hq, d = spec.num_tokens, spec.num_q_heads, spec.head_dim
     knobs = knobs_of(args, fgb)
     m = measure_pass(torch, fgb, spec, tens, dev, stream, knobs, args.steps, args.warmup,
-                     args.separate_append, args.kernel_events)
+                     args.separate_append, args.kernel_events, args.api)
     step, keep, kern, info = m["step"], m["keep"], m["kern"], m["info"]
     host_plan_s, ms_per_step = m["host_plan_s"], m["ms_per_step"]
 

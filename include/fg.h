@@ -230,6 +230,34 @@ fg_status fg_attention_ragged(const fg_plan* plan, void* d_meta,
                               void* out, int32_t out_dtype, float* lse,
                               void* d_ws, size_t ws_bytes, void* stream);
 
+/* fg_attention_ragged with this pass's own key positions (ctx_s .. ctx_s +
+ * q_len_s - 1 of each sequence) read from k_new / v_new ([T, Hkv, D] bf16, as
+ * given to fg_kv_append) instead of the pools: the pools need to hold only
+ * the cached context, and the pool slots of the new positions are never read.
+ * The attention step of fg_pass, for a pass whose K/V is not (yet) appended.
+ * Arguments and errors as for fg_attention_ragged; FG_E_INVALID for a null or
+ * misaligned k_new / v_new. */
+fg_status fg_attention_ragged_direct(const fg_plan* plan, void* d_meta, const void* q,
+                                     const void* k_new, const void* v_new,
+                                     const void* k_pool, const void* v_pool, void* out,
+                                     int32_t out_dtype, float* lse, void* d_ws, size_t ws_bytes,
+                                     void* stream);
+
+/* One whole pass: the plan's metadata upload, the KV append and the attention
+ * (plus the merge launch when the plan splits prefill tiles), with the append
+ * done by work-groups of the attention launch.  Attention reads key positions
+ * below each sequence's cached context from the pools and the pass's own
+ * positions straight from k_new / v_new, so it does not wait for the append;
+ * the pools hold the pass's K/V once the stream has passed the call, bit for
+ * bit as fg_kv_append writes them ("DeepSpeed-FastGen Guide: Dynamic SplitKV
+ * Serving", section "3. Paged KV Memory Management with Zero Overhead": the
+ * kernel reads the block tables itself, with no separate translation pass).
+ * Arguments as for fg_plan_upload, fg_kv_append and fg_attention_ragged
+ * (k_pool / v_pool are written); the same errors. */
+fg_status fg_pass(const fg_plan* plan, void* d_meta, const void* q, const void* k_new,
+                  const void* v_new, void* k_pool, void* v_pool, void* out, int32_t out_dtype,
+                  float* lse, void* d_ws, size_t ws_bytes, void* stream);
+
 /* fg_attention_ragged for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * allocation): the same kernels and results, bit for bit, with no workspace

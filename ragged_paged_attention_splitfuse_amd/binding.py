@@ -79,6 +79,11 @@ SIGNATURES = {
     "fg_attention_ragged": (ctypes.c_int32, [ctypes.c_void_p] * 6 + [ctypes.c_int32, ctypes.c_void_p,
                                                                      ctypes.c_void_p, ctypes.c_size_t,
                                                                      ctypes.c_void_p]),
+    "fg_attention_ragged_direct": (ctypes.c_int32, [ctypes.c_void_p] * 8 + [ctypes.c_int32, ctypes.c_void_p,
+                                                                            ctypes.c_void_p, ctypes.c_size_t,
+                                                                            ctypes.c_void_p]),
+    "fg_pass": (ctypes.c_int32, [ctypes.c_void_p] * 8 + [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                                         ctypes.c_size_t, ctypes.c_void_p]),
     "fg_attention_ragged_noalloc": (ctypes.c_int32, [ctypes.c_void_p] * 6 + [ctypes.c_int32, ctypes.c_void_p,
                                                                              ctypes.c_void_p]),
     "fg_noalloc_scratch_bytes": (ctypes.c_size_t, []),
@@ -324,6 +329,68 @@ def fg_attention_ragged(plan, d_meta, q, k_pool, v_pool, out, lse=None, workspac
     return workspace
 
 
+def _check_pass_tensors(plan, q, k_new, v_new, k_pool, v_pool, out, lse, out_dtype):
+    t, hq, hkv, d = plan.num_tokens, plan.num_q_heads, plan.num_kv_heads, plan.head_dim
+    kshape, vshape = pool_shapes(plan.num_blocks, hkv, plan.block_size, d)
+    _check_tensor(q, (t, hq, d), "bf16", "q")
+    _check_tensor(k_new, (t, hkv, d), "bf16", "k_new")
+    _check_tensor(v_new, (t, hkv, d), "bf16", "v_new")
+    _check_tensor(k_pool, kshape, "bf16", "k_pool")
+    _check_tensor(v_pool, vshape, "bf16", "v_pool")
+    _check_tensor(out, (t, hq, d), "bf16" if out_dtype == FG_DTYPE_BF16 else "f32", "out")
+    _check_tensor(lse, (t, hq), "f32", "lse")
+
+
+def _out_dtype(out, out_dtype):
+    if out_dtype is None:
+        import torch
+        out_dtype = FG_DTYPE_BF16 if (hasattr(out, "dtype") and out.dtype == torch.bfloat16) else FG_DTYPE_F32
+    return out_dtype
+
+
+def _workspace(plan, workspace, device="cuda"):
+    ws_bytes = plan.info["workspace_bytes"]
+    if workspace is None and ws_bytes > 0:
+        import torch
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
+    have = 0
+    if workspace is not None:
+        have = workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else ws_bytes
+    return workspace, have
+
+
+def fg_attention_ragged_direct(plan, d_meta, q, k_new, v_new, k_pool, v_pool, out, lse=None,
+                               workspace=None, stream=None, out_dtype=None):
+    """Attention with this pass's own K/V read from k_new / v_new (no append)."""
+    out_dtype = _out_dtype(out, out_dtype)
+    _check_pass_tensors(plan, q, k_new, v_new, k_pool, v_pool, out, lse, out_dtype)
+    workspace, have = _workspace(plan, workspace)
+    _check(lib().fg_attention_ragged_direct(plan.handle, _ptr(d_meta if d_meta is not None else plan.meta),
+                                            _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool),
+                                            _ptr(out), int(out_dtype), _ptr(lse), _ptr(workspace), int(have),
+                                            _stream(stream)), "fg_attention_ragged_direct")
+    return workspace
+
+
+def fg_pass(plan, d_meta, q, k_new, v_new, k_pool, v_pool, out, lse=None, workspace=None, stream=None,
+            out_dtype=None, device="cuda"):
+    """One whole pass (upload, append, attention); d_meta is allocated here
+    (torch uint8) when None.  Returns (d_meta, workspace)."""
+    if d_meta is None:
+        import torch
+        d_meta = torch.empty(max(16, plan.info["metadata_bytes"]), dtype=torch.uint8, device=device)
+    elif hasattr(d_meta, "numel") and d_meta.numel() * d_meta.element_size() < plan.info["metadata_bytes"]:
+        raise ValueError("metadata buffer too small")
+    out_dtype = _out_dtype(out, out_dtype)
+    _check_pass_tensors(plan, q, k_new, v_new, k_pool, v_pool, out, lse, out_dtype)
+    workspace, have = _workspace(plan, workspace, device)
+    _check(lib().fg_pass(plan.handle, _ptr(d_meta), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool),
+                         _ptr(v_pool), _ptr(out), int(out_dtype), _ptr(lse), _ptr(workspace), int(have),
+                         _stream(stream)), "fg_pass")
+    plan.meta = d_meta
+    return d_meta, workspace
+
+
 def fg_attention_ragged_noalloc(plan, d_meta, q, k_pool, v_pool, out, lse=None, stream=None,
                                 out_dtype=None):
     """fg_attention_ragged with the library's scratch array as its workspace
@@ -379,3 +446,5 @@ kv_append = fg_kv_append
 upload_append = fg_upload_append
 attention_ragged = fg_attention_ragged
 attention_ragged_noalloc = fg_attention_ragged_noalloc
+attention_ragged_direct = fg_attention_ragged_direct
+run_pass = fg_pass

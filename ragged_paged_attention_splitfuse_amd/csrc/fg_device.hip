@@ -67,6 +67,17 @@ struct AttnArgs {
   const uint16_t* q;
   const uint16_t* kpool;
   const uint16_t* vpool;
+  // When set, key positions at or past a sequence's cached context (this
+  // pass's own tokens) are read from k_new / v_new instead of the pools, so
+  // the attention does not depend on the append of the same pass.
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  // Fused append (fg_pass): work-groups n_items .. n_items + n_runs * hkv - 1
+  // of the attention launch append run (i / hkv) for kv head (i % hkv).
+  const RunRec* runs;
+  uint16_t* kpool_w;
+  uint16_t* vpool_w;
+  int32_t n_items;
   void* out;
   float* lse;
   float* ws_o;
@@ -98,6 +109,15 @@ __device__ __forceinline__ int vt_off(int d, int t) {
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ uint32_t pick_lo(uint32_t a, uint32_t b) {
+  // {a.lo, b.lo} as (low half, high half)
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pick_hi(uint32_t a, uint32_t b) {
+  // {a.hi, b.hi}
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
@@ -161,6 +181,28 @@ __device__ __forceinline__ u32x4 zero_tail(u32x4 v, int first, int valid) {
   return v;
 }
 
+// Row of k_new / v_new holding key position p (>= ctx) of a sequence.
+__device__ __forceinline__ size_t new_row(const AttnArgs& a, const SeqRec& sq, int p, int g) {
+  return size_t(sq.q_start + (p - sq.ctx)) * a.hkv + g;
+}
+
+// Replace the elements of an 8-token chunk of dim d (tokens first .. first+7)
+// at positions in [ctx, kv_len) by this pass's new V values.
+template <int D>
+__device__ __forceinline__ u32x4 patch_new_v(const AttnArgs& a, const SeqRec& sq, u32x4 v, int first,
+                                             int d, int g) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int t = first + e;
+    if (t >= sq.ctx && t < sq.kv_len) {
+      const uint32_t x = a.v_new[new_row(a, sq, t, g) * D + d];
+      const uint32_t w = v[e >> 1];
+      v[e >> 1] = (e & 1) ? ((w & 0x0000ffffu) | (x << 16)) : ((w & 0xffff0000u) | x);
+    }
+  }
+  return v;
+}
+
 // Destination of packed row r of an item: final (token, head) row or a
 // partial row of the workspace.
 __device__ __forceinline__ void store_result(const AttnArgs& a, const SeqRec& sq, const ItemRec& it,
@@ -209,7 +251,7 @@ __device__ __forceinline__ float load_partial(const float* p) {
 // (ST = 32 or 64: one or two 32-token V^T sub-blocks) with its own
 // online-softmax state; the four states merge at the end.
 // LDS use: per-wave probability exchange, then the cross-wave merge buffers.
-template <int D, int B, int NR, int ST>
+template <int D, int B, int NR, int ST, bool DIRECT>
 __device__ void valu_item(const AttnArgs& a, const ItemRec& it, float* smem) {
   static_assert(ST % kValuSubTile == 0 && kKvTile % ST == 0, "whole sub-blocks per step");
   constexpr int LPT = D / 8;                // lanes holding one 16-byte-chunked K row
@@ -250,7 +292,26 @@ __device__ void valu_item(const AttnArgs& a, const ItemRec& it, float* smem) {
   }
   float* pbuf = smem + wave * (NR * ST);
 
-  for (int t0 = it.kv0 + wave * ST; t0 < it.kv1; t0 += kWaves * ST) {
+  // With k_new / v_new (fused pass) the pool stream stops at ctx and this
+  // pass's own positions are taken one token at a time after the loop; the
+  // wavefront's first such token is loaded here, before the stream, so its
+  // latency overlaps the loop (K chunk kdc, and the dims vd + 16 i of V as
+  // bf16 pairs).
+  const int main_end = DIRECT ? min(kv_valid, sq.ctx) : kv_valid;
+  const int p_tail = max(it.kv0, sq.ctx) + wave;
+  u32x4 kn_pre = u32x4{0u, 0u, 0u, 0u};
+  uint32_t vn_pre[UV / 2];
+#pragma unroll
+  for (int i = 0; i < UV / 2; ++i) vn_pre[i] = 0u;
+  if (DIRECT && p_tail < it.kv1) {
+    const size_t nrow = new_row(a, sq, p_tail, g) * D;
+    kn_pre = ld16(a.k_new + nrow + 8 * kdc);
+#pragma unroll
+    for (int i = 0; i < UV / 2; ++i)
+      vn_pre[i] = uint32_t(a.v_new[nrow + vd + 32 * i]) | (uint32_t(a.v_new[nrow + vd + 32 * i + 16]) << 16);
+  }
+  const int kv_hi = min(it.kv1, main_end);
+  for (int t0 = it.kv0 + wave * ST; t0 < kv_hi; t0 += kWaves * ST) {
     u32x4 kr[UK], vr[HV][UV];
     int blk_u = 0;
     if constexpr (B >= ST) blk_u = win.get(t0 / B);
@@ -258,7 +319,7 @@ __device__ void valu_item(const AttnArgs& a, const ItemRec& it, float* smem) {
     for (int i = 0; i < UK; ++i) {
       const int tok = t0 + i * TPI + ktok;
       kr[i] = u32x4{0u, 0u, 0u, 0u};
-      if (tok < kv_valid) {
+      if (tok < main_end) {
         const int blk = (B >= ST) ? blk_u : bt[tok / B];
         // Each K and V^T load instruction reads whole 128-byte lines (TPI full
         // K rows; 16 dims of one V^T sub-block) that no other load of this
@@ -272,14 +333,14 @@ __device__ void valu_item(const AttnArgs& a, const ItemRec& it, float* smem) {
 #pragma unroll
       for (int i = 0; i < UV; ++i) {
         vr[h][i] = u32x4{0u, 0u, 0u, 0u};
-        if (vt < kv_valid) {
+        if (vt < main_end) {
           const int blk = (B >= ST) ? blk_u : bt[vt / B];
           vr[h][i] = ld16_nt(a.vpool + (size_t(blk) * a.hkv + g) * D * B + vt_off<D, B>(vd + 16 * i, vt % B));
         }
       }
-      if (vt < kv_valid && vt + 8 > kv_valid) {
+      if (vt < main_end && vt + 8 > main_end) {
 #pragma unroll
-        for (int i = 0; i < UV; ++i) vr[h][i] = zero_tail(vr[h][i], vt, kv_valid);
+        for (int i = 0; i < UV; ++i) vr[h][i] = zero_tail(vr[h][i], vt, main_end);
       }
     }
 
@@ -294,7 +355,7 @@ __device__ void valu_item(const AttnArgs& a, const ItemRec& it, float* smem) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) p = dot2(q[r][e], kr[i][e], p);
         p = group_sum<LPT>(p);
-        s[r][i] = (tok < it.kv1 && tok <= lim[r]) ? p * a.scale_log2 : -INFINITY;
+        s[r][i] = (tok < kv_hi && tok <= lim[r]) ? p * a.scale_log2 : -INFINITY;
       }
     }
 
@@ -360,6 +421,48 @@ __device__ void valu_item(const AttnArgs& a, const ItemRec& it, float* smem) {
 #pragma unroll
           for (int u = 0; u < 8; ++u) t = fmaf(pp[h][r][u], v[u], t);
           acc[r][i] = t;
+        }
+      }
+    }
+  }
+
+  // This pass's own positions [max(kv0, ctx), kv1) (fused pass only; one token
+  // for a decode, at most kValuMaxRows for a tiny chunk): wavefront w takes
+  // tokens w, w + 4, ...  Every lane reads chunk kdc of the K row, so each
+  // LPT-lane group holds the full score; the weight enters l in the first
+  // group's lanes and acc in the vtc == 0 lanes only, as the reductions below
+  // sum over token groups and over the four vtc lanes.
+  if constexpr (DIRECT) {
+    for (int p = p_tail; p < it.kv1; p += kWaves) {
+      u32x4 kn = kn_pre;
+      float vv[UV];
+      if (p == p_tail) {
+#pragma unroll
+        for (int i = 0; i < UV / 2; ++i) {
+          vv[2 * i] = bf_lo(vn_pre[i]);
+          vv[2 * i + 1] = bf_hi(vn_pre[i]);
+        }
+      } else {
+        const size_t nrow = new_row(a, sq, p, g) * D;
+        kn = ld16(a.k_new + nrow + 8 * kdc);
+#pragma unroll
+        for (int i = 0; i < UV; ++i) vv[i] = __uint_as_float(uint32_t(a.v_new[nrow + vd + 16 * i]) << 16);
+      }
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        float sc = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sc = dot2(q[r][e], kn[e], sc);
+        sc = group_sum<LPT>(sc);
+        const float x = p <= lim[r] ? sc * a.scale_log2 : -INFINITY;
+        const float mn = fmaxf(m[r], x);
+        if (mn != -INFINITY) {
+          const float alpha = fast_exp2(m[r] - mn);
+          const float w = fast_exp2(x - mn);
+          l[r] = l[r] * alpha + (ktok == 0 ? w : 0.f);
+#pragma unroll
+          for (int i = 0; i < UV; ++i) acc[r][i] = acc[r][i] * alpha + (vtc == 0 ? w * vv[i] : 0.f);
+          m[r] = mn;
         }
       }
     }
@@ -451,7 +554,7 @@ __device__ __forceinline__ void lds_dma16(const uint16_t* src, uint16_t* lds_seg
   __builtin_amdgcn_global_load_lds((gptr)src, (lptr)lds_seg, 16, 0, 0);
 }
 
-template <int D, int B>
+template <int D, int B, bool DIRECT>
 __device__ void mfma_item(const AttnArgs& a, const ItemRec& it, uint16_t* lds) {
   using L = MfmaLds<D>;
   constexpr int CPR = D / 8;                          // 16-byte chunks per K row
@@ -501,7 +604,9 @@ __device__ void mfma_item(const AttnArgs& a, const ItemRec& it, uint16_t* lds) {
       const int ch = tid + kThreads * c;
       const int tok = ch / CPR, dc = ch % CPR, p = tb + tok;
       kst[c] = u32x4{0u, 0u, 0u, 0u};
-      if (full || p < kv_valid) {
+      if (DIRECT && p >= sq.ctx && p < kv_valid) {
+        kst[c] = ld16(a.k_new + new_row(a, sq, p, g) * D + 8 * dc);
+      } else if (full || p < kv_valid) {
         const int blk = bt[p / B];
         kst[c] = ld16(a.kpool + ((size_t(blk) * a.hkv + kv_head_base) * B + p % B) * D + 8 * dc);
       }
@@ -515,6 +620,7 @@ __device__ void mfma_item(const AttnArgs& a, const ItemRec& it, uint16_t* lds) {
         const int blk = bt[p / B];
         vst[c] = ld16(a.vpool + (size_t(blk) * a.hkv + kv_head_base) * D * B + vt_off<D, B>(d, p % B));
         if (!full && p + 8 > kv_valid) vst[c] = zero_tail(vst[c], p, kv_valid);
+        if (DIRECT && p + 8 > sq.ctx) vst[c] = patch_new_v<D>(a, sq, vst[c], p, d, g);
       }
     }
   };
@@ -575,17 +681,70 @@ __device__ void mfma_item(const AttnArgs& a, const ItemRec& it, uint16_t* lds) {
   }
   BlockWindow win{bt, sq.nblk, 0, 0};
   if constexpr (B == kKvTile) win.load(it.kv0 / B);
+  // This pass's own tokens (positions >= ctx), when read from k_new / v_new:
+  // their K rows are DMA'd from k_new (each lane picks its token's row), and
+  // their V, token-major there, goes through registers and is transposed into
+  // the V^T stage: thread u < 16 * D / 8 takes tokens 4 (u / (D/8)) .. +3 of
+  // dims 8 (u % (D/8)) .. +7 (four 16-byte loads, issued a stage ahead like the
+  // DMA) and writes 8 dims x 4 tokens.  A stage wholly past ctx skips the V DMA;
+  // the one stage holding ctx takes its V DMA from the pool and overwrites the
+  // positions >= ctx once every wave's DMA has landed (one extra barrier).
+  constexpr bool direct = DIRECT;
+  constexpr int VN_DG = D / 8;
+  const int vn_tg = tid / VN_DG, vn_dg = tid % VN_DG;
+  const bool vn_thread = tid < 16 * VN_DG;
+  u32x4 vnew[4];
+  auto load_vnew = [&](int tb) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int p = tb + 4 * vn_tg + k;
+      vnew[k] = u32x4{0u, 0u, 0u, 0u};
+      if (vn_thread && p >= sq.ctx && p < kv_valid) vnew[k] = ld16(a.v_new + new_row(a, sq, p, g) * D + 8 * vn_dg);
+    }
+  };
+  auto store_vnew = [&](int tb, int buf) {
+    if (!vn_thread) return;
+    uint16_t* vt = lds + buf * L::STAGE + L::KT;
+    const int p0 = tb + 4 * vn_tg;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const uint32_t w0 = (d & 1) ? pick_hi(vnew[0][d >> 1], vnew[1][d >> 1]) : pick_lo(vnew[0][d >> 1], vnew[1][d >> 1]);
+      const uint32_t w1 = (d & 1) ? pick_hi(vnew[2][d >> 1], vnew[3][d >> 1]) : pick_lo(vnew[2][d >> 1], vnew[3][d >> 1]);
+      uint16_t* dst = vt + (8 * vn_dg + d) * L::VS + 4 * vn_tg;
+      if (p0 >= sq.ctx) {
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        *reinterpret_cast<u32x2*>(dst) = u32x2{w0, w1};
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (p0 + k >= sq.ctx) dst[k] = uint16_t(((k < 2 ? w0 : w1) >> (16 * (k & 1))) & 0xffffu);
+      }
+    }
+  };
   auto dma_stage = [&](int tb, int buf) {
     const size_t tile = (size_t(win.get(tb / B)) * a.hkv + kv_head_base) * (size_t(B) * D);
     uint16_t* kt = lds + buf * L::STAGE;
     uint16_t* vt = kt + L::KT;
+    const bool has_new = direct && tb + kKvTile > sq.ctx;
 #pragma unroll
-    for (int i = 0; i < KSEG_W; ++i)
-      if (i * kWaves + wave < K_SEGS) lds_dma16(a.kpool + tile + koff[i], kt + (i * kWaves + wave) * 512);
+    for (int i = 0; i < KSEG_W; ++i) {
+      if (i * kWaves + wave < K_SEGS) {
+        const uint16_t* src = a.kpool + tile + koff[i];
+        if (has_new) {
+          const int p = tb + koff[i] / D;
+          if (p >= sq.ctx && p < kv_valid) src = a.k_new + new_row(a, sq, p, g) * D + koff[i] % D;
+        }
+        lds_dma16(src, kt + (i * kWaves + wave) * 512);
+      }
+    }
+    if (!(has_new && tb >= sq.ctx)) {
 #pragma unroll
-    for (int i = 0; i < VSEG_W; ++i)
-      if (i * kWaves + wave < V_SEGS) lds_dma16(a.vpool + tile + voff[i], vt + (i * kWaves + wave) * 512);
+      for (int i = 0; i < VSEG_W; ++i)
+        if (i * kWaves + wave < V_SEGS) lds_dma16(a.vpool + tile + voff[i], vt + (i * kWaves + wave) * 512);
+    }
+    if (has_new) load_vnew(tb);
   };
+
   auto fix_v_tail = [&](int tb, int buf) {
     if (tb + kKvTile <= kv_valid) return;
     uint16_t* vt = lds + buf * L::STAGE + L::KT;
@@ -599,10 +758,18 @@ __device__ void mfma_item(const AttnArgs& a, const ItemRec& it, uint16_t* lds) {
       }
     }
   };
-  if constexpr (B == kKvTile) {
+  // After this wave's DMA of stage tb has landed: zero DMA'd V past kv_len and
+  // put this pass's V into the positions >= ctx.
+  auto finish_stage = [&](int tb, int buf) {
+    if (!(direct && tb >= sq.ctx)) fix_v_tail(tb, buf);
+    if (direct && tb + kKvTile > sq.ctx) {
+      if (tb < sq.ctx) __syncthreads();
+      store_vnew(tb, buf);
+    }
+  };  if constexpr (B == kKvTile) {
     dma_stage(it.kv0, 0);
     __builtin_amdgcn_s_waitcnt(0);
-    fix_v_tail(it.kv0, 0);
+    finish_stage(it.kv0, 0);
   } else {
     load_stage(it.kv0);
     store_stage(0);
@@ -714,7 +881,7 @@ __device__ void mfma_item(const AttnArgs& a, const ItemRec& it, uint16_t* lds) {
     if (t + 1 < ntiles) {
       if constexpr (B == kKvTile) {
         __builtin_amdgcn_s_waitcnt(0);
-        fix_v_tail(tb + kKvTile, (t + 1) & 1);
+        finish_stage(tb + kKvTile, (t + 1) & 1);
       } else {
         store_stage((t + 1) & 1);
       }
@@ -859,40 +1026,6 @@ __device__ void finish_split(const AttnArgs& a, const ItemRec& it, int* last_fla
     __hip_atomic_store(a.counters + it.group, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The decode loop's step: in the kernel that also runs matrix-core tiles the
-// tile path sets the register budget, and 64-token steps (twice the loads in
-// flight per wavefront) fit inside it; the decode-only kernel keeps 32-token
-// steps, whose smaller register count lets a CU hold a third work-group.
-template <int D, int B, bool MFMA>
-__global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
-  constexpr int kStep = MFMA ? 2 * kValuSubTile : kValuSubTile;
-  constexpr int kLds = MFMA ? (MfmaLds<D>::BYTES > valu_lds_bytes<D, kStep>() ? MfmaLds<D>::BYTES
-                                                                               : valu_lds_bytes<D, kStep>())
-                            : valu_lds_bytes<D, kStep>();
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kLds];
-  const ItemRec it = a.items[blockIdx.x];
-  if constexpr (MFMA) {
-    if (it.waves > 0) {
-      mfma_item<D, B>(a, it, reinterpret_cast<uint16_t*>(smem));
-      if (it.group >= 0 && it.group < a.n_inlaunch) finish_split<D>(a, it, reinterpret_cast<int*>(smem));
-      return;
-    }
-  }
-  if (it.nrows == 1)
-    valu_item<D, B, 1, kStep>(a, it, reinterpret_cast<float*>(smem));
-  else
-    valu_item<D, B, kValuMaxRows, kStep>(a, it, reinterpret_cast<float*>(smem));
-  if (it.group >= 0 && it.group < a.n_inlaunch) finish_split<D>(a, it, reinterpret_cast<int*>(smem));
-}
-
-// Merge launch for split prefill tiles: one work-group per group, after the
-// attention launch (so plain loads see the partial rows).
-template <int D>
-__global__ __launch_bounds__(kThreads) void merge_kernel(AttnArgs a) {
-  __shared__ float red[2 * kMfmaTileRows];
-  merge_group<D, false>(a, a.groups[a.n_inlaunch + blockIdx.x], red);
-}
-
 // Append of one run (up to B consecutive new tokens of one sequence in one
 // block) for one kv head.  K rows are copied with 16-byte loads and stores.
 // V is written transposed: a thread takes an aligned group of 8 block slots
@@ -901,14 +1034,6 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(AttnArgs a) {
 // contiguous 16-byte slot runs, one per dim; groups the run only partly covers
 // store their valid slots with 2-byte stores, so no byte outside the run is
 // written.
-__device__ __forceinline__ uint32_t pick_lo(uint32_t a, uint32_t b) {
-  // {a.lo, b.lo} as (low half, high half)
-  return __builtin_amdgcn_perm(b, a, 0x05040100u);
-}
-__device__ __forceinline__ uint32_t pick_hi(uint32_t a, uint32_t b) {
-  // {a.hi, b.hi}
-  return __builtin_amdgcn_perm(b, a, 0x07060302u);
-}
 
 template <int D, int B>
 __device__ __forceinline__ void append_run(const RunRec run, const int g, const uint16_t* k_new,
@@ -960,6 +1085,50 @@ __device__ __forceinline__ void append_run(const RunRec run, const int g, const 
       }
     }
   }
+}
+
+// The decode loop's step: in the kernel that also runs matrix-core tiles the
+// tile path sets the register budget, and 64-token steps (twice the loads in
+// flight per wavefront) fit inside it; the decode-only kernel keeps 32-token
+// steps, whose smaller register count lets a CU hold a third work-group.
+template <int D, int B, bool MFMA, bool DIRECT>
+__global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
+  constexpr int kStep = MFMA ? 2 * kValuSubTile : kValuSubTile;
+  constexpr int kLds = MFMA ? (MfmaLds<D>::BYTES > valu_lds_bytes<D, kStep>() ? MfmaLds<D>::BYTES
+                                                                               : valu_lds_bytes<D, kStep>())
+                            : valu_lds_bytes<D, kStep>();
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kLds];
+  if constexpr (DIRECT) {
+    if (int(blockIdx.x) >= a.n_items) {
+      // fused append: reads k_new / v_new and writes pool slots at positions
+      // >= ctx, which no attention item of this launch reads from the pools
+      const unsigned w = blockIdx.x - unsigned(a.n_items);
+      append_run<D, B>(a.runs[w / unsigned(a.hkv)], int(w % unsigned(a.hkv)), a.k_new, a.v_new,
+                       a.kpool_w, a.vpool_w, a.hkv);
+      return;
+    }
+  }
+  const ItemRec it = a.items[blockIdx.x];
+  if constexpr (MFMA) {
+    if (it.waves > 0) {
+      mfma_item<D, B, DIRECT>(a, it, reinterpret_cast<uint16_t*>(smem));
+      if (it.group >= 0 && it.group < a.n_inlaunch) finish_split<D>(a, it, reinterpret_cast<int*>(smem));
+      return;
+    }
+  }
+  if (it.nrows == 1)
+    valu_item<D, B, 1, kStep, DIRECT>(a, it, reinterpret_cast<float*>(smem));
+  else
+    valu_item<D, B, kValuMaxRows, kStep, DIRECT>(a, it, reinterpret_cast<float*>(smem));
+  if (it.group >= 0 && it.group < a.n_inlaunch) finish_split<D>(a, it, reinterpret_cast<int*>(smem));
+}
+
+// Merge launch for split prefill tiles: one work-group per group, after the
+// attention launch (so plain loads see the partial rows).
+template <int D>
+__global__ __launch_bounds__(kThreads) void merge_kernel(AttnArgs a) {
+  __shared__ float red[2 * kMfmaTileRows];
+  merge_group<D, false>(a, a.groups[a.n_inlaunch + blockIdx.x], red);
 }
 
 // One work-group per (append run, kv head).
@@ -1207,7 +1376,8 @@ namespace {
 // the plan.  `profile` allows the per-launch HIP events of fg_profile_enable.
 fg_status launch_attention(const fg_plan* plan, void* d_meta, const void* q, const void* k_pool,
                            const void* v_pool, void* out, int32_t out_dtype, float* lse, void* d_ws,
-                           hipStream_t s, bool profile) {
+                           hipStream_t s, bool profile, const void* k_new = nullptr,
+                           const void* v_new = nullptr, bool fused_append = false) {
   uint8_t* meta = static_cast<uint8_t*>(d_meta);
   AttnArgs a;
   a.seqs = reinterpret_cast<const SeqRec*>(meta + plan->off_seqs);
@@ -1218,6 +1388,12 @@ fg_status launch_attention(const fg_plan* plan, void* d_meta, const void* q, con
   a.q = static_cast<const uint16_t*>(q);
   a.kpool = static_cast<const uint16_t*>(k_pool);
   a.vpool = static_cast<const uint16_t*>(v_pool);
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.runs = reinterpret_cast<const RunRec*>(meta + plan->off_runs);
+  a.kpool_w = static_cast<uint16_t*>(const_cast<void*>(k_pool));
+  a.vpool_w = static_cast<uint16_t*>(const_cast<void*>(v_pool));
+  a.n_items = plan->n_items;
   a.out = out;
   a.lse = lse;
   a.ws_o = plan->ws_bytes ? reinterpret_cast<float*>(static_cast<uint8_t*>(d_ws) + plan->ws_o_off) : nullptr;
@@ -1232,13 +1408,21 @@ fg_status launch_attention(const fg_plan* plan, void* d_meta, const void* q, con
 
   {
     ProfScope prof(profile ? FG_KERNEL_ATTENTION : FG_KERNEL_COUNT, s);
-    const dim3 grid(unsigned(plan->n_items));
+    const unsigned n_append = fused_append ? unsigned(plan->n_runs) * unsigned(plan->hkv) : 0u;
+    const dim3 grid(unsigned(plan->n_items) + n_append);
 #define FG_LAUNCH_ATTN(D_, B_)                                                                 \
   do {                                                                                         \
-    if (plan->n_mfma > 0)                                                                      \
-      hipLaunchKernelGGL((attn_kernel<D_, B_, true>), grid, dim3(kThreads), 0, s, a);          \
-    else                                                                                       \
-      hipLaunchKernelGGL((attn_kernel<D_, B_, false>), grid, dim3(kThreads), 0, s, a);         \
+    if (a.k_new) {                                                                             \
+      if (plan->n_mfma > 0)                                                                    \
+        hipLaunchKernelGGL((attn_kernel<D_, B_, true, true>), grid, dim3(kThreads), 0, s, a);  \
+      else                                                                                     \
+        hipLaunchKernelGGL((attn_kernel<D_, B_, false, true>), grid, dim3(kThreads), 0, s, a); \
+    } else {                                                                                   \
+      if (plan->n_mfma > 0)                                                                    \
+        hipLaunchKernelGGL((attn_kernel<D_, B_, true, false>), grid, dim3(kThreads), 0, s, a); \
+      else                                                                                     \
+        hipLaunchKernelGGL((attn_kernel<D_, B_, false, false>), grid, dim3(kThreads), 0, s, a);\
+    }                                                                                          \
   } while (0)
     FG_SWITCH_DB(plan->head_dim, plan->block_size, FG_LAUNCH_ATTN);
 #undef FG_LAUNCH_ATTN
@@ -1331,6 +1515,49 @@ extern "C" fg_status fg_attention_ragged_noalloc(const fg_plan* plan, void* d_me
 }
 
 extern "C" size_t fg_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+extern "C" fg_status fg_attention_ragged_direct(const fg_plan* plan, void* d_meta, const void* q,
+                                                const void* k_new, const void* v_new,
+                                                const void* k_pool, const void* v_pool, void* out,
+                                                int32_t out_dtype, float* lse, void* d_ws,
+                                                size_t ws_bytes, void* stream) {
+  if (!plan) return FG_E_INVALID;
+  if (out_dtype != FG_DTYPE_F32 && out_dtype != FG_DTYPE_BF16) return FG_E_UNSUPPORTED;
+  if (plan->n_items == 0) return FG_OK;
+  const fg_status st = check_attention_args(plan, out_dtype, d_meta, q, k_pool, v_pool, out, lse);
+  if (st != FG_OK) return st;
+  if (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new)) return FG_E_INVALID;
+  if (plan->ws_bytes > 0 && (!d_ws || ws_bytes < plan->ws_bytes || !aligned16(d_ws)))
+    return FG_E_WORKSPACE;
+  return launch_attention(plan, d_meta, q, k_pool, v_pool, out, out_dtype, lse, d_ws,
+                          static_cast<hipStream_t>(stream), true, k_new, v_new, false);
+}
+
+extern "C" fg_status fg_pass(const fg_plan* plan, void* d_meta, const void* q, const void* k_new,
+                             const void* v_new, void* k_pool, void* v_pool, void* out,
+                             int32_t out_dtype, float* lse, void* d_ws, size_t ws_bytes, void* stream) {
+  if (!plan) return FG_E_INVALID;
+  if (out_dtype != FG_DTYPE_F32 && out_dtype != FG_DTYPE_BF16) return FG_E_UNSUPPORTED;
+  if (plan->n_items == 0) return FG_OK;
+  fg_status st = check_attention_args(plan, out_dtype, d_meta, q, k_pool, v_pool, out, lse);
+  if (st != FG_OK) return st;
+  if (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new)) return FG_E_INVALID;
+  if (plan->ws_bytes > 0 && (!d_ws || ws_bytes < plan->ws_bytes || !aligned16(d_ws)))
+    return FG_E_WORKSPACE;
+  if (plan->n_tiles > 0) {
+    // Prefill tiles: their stages over the pass's own tokens measured slower
+    // when staged from k_new / v_new than from the pool (the V transpose goes
+    // through registers), so the append runs first, fused with the upload.
+    st = fg_upload_append(plan, d_meta, k_new, v_new, k_pool, v_pool, stream);
+    if (st != FG_OK) return st;
+    return launch_attention(plan, d_meta, q, k_pool, v_pool, out, out_dtype, lse, d_ws,
+                            static_cast<hipStream_t>(stream), true);
+  }
+  st = fg_plan_upload(plan, d_meta, stream);
+  if (st != FG_OK) return st;
+  return launch_attention(plan, d_meta, q, k_pool, v_pool, out, out_dtype, lse, d_ws,
+                          static_cast<hipStream_t>(stream), true, k_new, v_new, true);
+}
 
 extern "C" fg_status fg_profile_enable(int32_t mask) {
   std::lock_guard<std::mutex> lk(g_prof_mu);

@@ -389,7 +389,9 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
       return items;
     };
     int64_t total_items = split_all(target);
-    if (total_items > kMaxGroupsPerLaunch) return FG_E_RANGE;
+    if (total_items > kMaxGroupsPerLaunch ||
+        total_items + int64_t(runs.size()) * d->num_kv_heads > kMaxGroupsPerLaunch)
+      return FG_E_RANGE;   // attention items, and attention items + fused append groups
     // Round fitting (see kRoundFitSlack): a tile-free plan just past a whole
     // number of work-group rounds gets a larger target until it fits them.
     if (d->force_splits == 0 && d->split_policy == FG_SPLIT_BALANCED && tile_groups == 0) {
@@ -486,6 +488,8 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
     plan->n_runs = int32_t(runs.size());
     plan->n_mfma = int32_t(mfma.size());
     plan->n_valu = int32_t(valu.size());
+    plan->n_tiles = int32_t(std::count_if(mfma.begin(), mfma.end(),
+                                          [](const Pending& x) { return x.item.waves >= 2; }));
     plan->n_items = plan->n_mfma + plan->n_valu;
     plan->n_merge_groups = int32_t(merges.size());
     plan->n_inlaunch_groups = n_inl;

@@ -26,6 +26,7 @@ struct fg_plan {
   int32_t n_items = 0;   // n_mfma matrix-core items first, then n_valu
   int32_t n_mfma = 0;
   int32_t n_valu = 0;
+  int32_t n_tiles = 0;   // matrix-core items of two or more wavefronts (prefill tiles)
   int32_t n_merge_groups = 0;   // row groups that were split (one MergeRec each)
   int32_t n_inlaunch_groups = 0;  // the first of them, merged inside the attention launch
   int32_t n_partial_rows = 0;

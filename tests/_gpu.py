@@ -45,29 +45,44 @@ def fill_history(spec, tens, kp, vp):
     plan.close()
 
 
-def run_pass(spec, tens, kp, vp, out_dtype=torch.float32, dev_inputs=None, **knobs):
-    """Plan, upload, append and attend one pass; returns (out, lse, plan)."""
+MODES = ("separate", "pass", "direct")
+
+
+def run_pass(spec, tens, kp, vp, out_dtype=torch.float32, dev_inputs=None, mode="separate", **knobs):
+    """Plan and run one pass; returns (out, lse, plan).
+
+    mode "separate": fg_plan_upload, fg_kv_append, fg_attention_ragged;
+    "pass": fg_pass (upload, append and attention, the append inside the
+    attention launch); "direct": fg_plan_upload and fg_attention_ragged_direct
+    only -- the pools keep whatever the new positions held (poison in the
+    tests), since that call reads the pass's own K/V from k_new / v_new."""
     knobs.setdefault("target_cus", 0)
     plan = fgb.Plan.from_spec(spec, **knobs)
-    meta = plan.upload()
     if dev_inputs is None:
         dev_inputs = (to_dev(tens.q), to_dev(tens.k_new), to_dev(tens.v_new))
     q, kn, vn = dev_inputs
-    fgb.kv_append(plan, meta, kn, vn, kp, vp)
     t, hq, d = spec.num_tokens, spec.num_q_heads, spec.head_dim
     out = torch.full((t, hq, d), float("nan"), dtype=out_dtype, device="cuda")
     lse = torch.full((t, hq), float("nan"), dtype=torch.float32, device="cuda")
-    fgb.attention_ragged(plan, meta, q, kp, vp, out, lse)
+    if mode == "pass":
+        fgb.run_pass(plan, None, q, kn, vn, kp, vp, out, lse)
+    elif mode == "direct":
+        meta = plan.upload()
+        fgb.attention_ragged_direct(plan, meta, q, kn, vn, kp, vp, out, lse)
+    else:
+        meta = plan.upload()
+        fgb.kv_append(plan, meta, kn, vn, kp, vp)
+        fgb.attention_ragged(plan, meta, q, kp, vp, out, lse)
     torch.cuda.synchronize()
     return out, lse, plan
 
 
-def full_gpu_pass(spec, tens=None, poison=True, out_dtype=torch.float32, **knobs):
+def full_gpu_pass(spec, tens=None, poison=True, out_dtype=torch.float32, mode="separate", **knobs):
     if tens is None:
         tens = wl.make_tensors(spec)
     kp, vp = gpu_pools(spec, poison)
     fill_history(spec, tens, kp, vp)
-    out, lse, plan = run_pass(spec, tens, kp, vp, out_dtype=out_dtype, **knobs)
+    out, lse, plan = run_pass(spec, tens, kp, vp, out_dtype=out_dtype, mode=mode, **knobs)
     return tens, kp, vp, out, lse, plan
 
 

@@ -80,15 +80,56 @@ RANDOM_CASES = int(os.environ.get("FG_RANDOM_CASES", "48"))
 
 @pytest.mark.parametrize("seed", range(RANDOM_CASES))
 def test_random_compositions_match_oracle(seed):
+    # seeds cycle through the three ways of running a pass (see tests/_gpu.py)
     from tests._random_passes import random_pass
     spec, knobs = random_pass(seed)
-    _log(f"[case] random {seed}: S={spec.num_seqs} T={spec.num_tokens} q={[int(x) for x in spec.q_lens]} "
+    mode = G.MODES[seed % 3]
+    _log(f"[case] random {seed} ({mode}): S={spec.num_seqs} T={spec.num_tokens} q={[int(x) for x in spec.q_lens]} "
          f"ctx={[int(x) for x in spec.ctx_lens]} Hq/Hkv/D/B={spec.num_q_heads}/{spec.num_kv_heads}/"
          f"{spec.head_dim}/{spec.block_size} {knobs}")
-    tens, _, _, out, lse, plan = G.full_gpu_pass(spec, **knobs)
+    tens, kp, vp, out, lse, plan = G.full_gpu_pass(spec, mode=mode, **knobs)
     check_plan(plan, spec)
     o_ref, l_ref = G.oracle_pass(spec, tens)
-    compare(out, lse, o_ref, l_ref, f"random {seed}")
+    compare(out, lse, o_ref, l_ref, f"random {seed} ({mode})")
+    if mode == "pass":
+        kref, vref = oracle_pools(spec, tens, poison=True)
+        assert np.array_equal(G.to_host_bits(kp), kref) and np.array_equal(G.to_host_bits(vp), vref)
+
+
+@pytest.mark.parametrize("name", sorted(SMALL_SPECS))
+@pytest.mark.parametrize("mode", ["pass", "direct"])
+def test_single_launch_pass_and_direct_attention(name, mode):
+    # fg_pass: pools bit-exact (the append runs inside the attention launch)
+    # and attention on the oracle.  fg_attention_ragged_direct: the pools hold
+    # only the history, their new slots stay NaN-poisoned, so a read of one
+    # would show as a non-finite output.
+    spec = SMALL_SPECS[name]()
+    _log(f"[case] {mode} {name}")
+    tens, kp, vp, out, lse, plan = G.full_gpu_pass(spec, mode=mode)
+    o_ref, l_ref = G.oracle_pass(spec, tens)
+    compare(out, lse, o_ref, l_ref, f"{mode} {name}")
+    kref, vref = oracle_pools(spec, tens, poison=True)
+    if mode == "pass":
+        assert np.array_equal(G.to_host_bits(kp), kref) and np.array_equal(G.to_host_bits(vp), vref)
+    else:
+        # only the history was written: the new positions still hold poison
+        hk, hv = oracle_pools(spec, wl.PassTensors(q=tens.q, k_new=np.full_like(tens.k_new, wl.BF16_NAN),
+                                                   v_new=np.full_like(tens.v_new, wl.BF16_NAN),
+                                                   hist_k=tens.hist_k, hist_v=tens.hist_v), poison=True)
+        assert np.array_equal(G.to_host_bits(kp), hk) and np.array_equal(G.to_host_bits(vp), hv)
+
+
+@pytest.mark.parametrize("mode", ["pass", "direct"])
+@pytest.mark.parametrize("splits", [3, 64])
+def test_single_launch_pass_with_split_groups(mode, splits):
+    # split decode groups (merged in the attention launch) and split tiles
+    # (merge launch), with the pass's own tokens read from k_new / v_new
+    spec = SMALL_SPECS["gqa8_d128_b64_mixed"]()
+    _log(f"[case] {mode} force_splits={splits}")
+    tens, kp, vp, out, lse, plan = G.full_gpu_pass(spec, mode=mode, force_splits=splits, target_cus=16)
+    assert plan.info["num_merge_groups"] > 0
+    o_ref, l_ref = G.oracle_pass(spec, tens)
+    compare(out, lse, o_ref, l_ref, f"{mode} force_splits={splits}")
 
 
 # FG_RANDOM_BIG_CASES widens this one too (for example 400).
@@ -367,6 +408,41 @@ def test_one_hot_probe_block_boundaries(name, splits):
     assert float(np.max(np.abs(lse - score))) <= 1e-4
 
 
+@pytest.mark.parametrize("name", sorted(ONE_HOT_CASES))
+def test_one_hot_probe_on_new_tokens_direct(name):
+    # Addressing of k_new / v_new rows, bit for bit: the single key with
+    # K[.][0] = 40 is one of the pass's own tokens (position ctx + n // 2 of
+    # each sequence; a decode's own token), the pools hold only the history
+    # (new slots poisoned), and fg_attention_ragged_direct must give O =
+    # V[t*] exactly for every row at or past the target.
+    hq, hkv, d, b = ONE_HOT_CASES[name]
+    q_lens = [1, 70, 1, 3, 40, 1, 130, 2]
+    ctx = [b - 1, 0, 2 * b, 3 * b + 5, b, 5 * b - 1, 37, 64]
+    spec = wl.custom_spec("probe-new", q_lens, ctx, hq, hkv, d, b, seed=52)
+    _log(f"[case] one-hot probe on new tokens {name}")
+    base = wl.make_tensors(spec)
+    t_rows = spec.num_tokens
+    q = np.zeros((t_rows, hq, d), np.float32)
+    q[:, :, 0] = 40.0
+    kn = np.zeros((t_rows, hkv, d), np.float32)
+    cu = np.concatenate([[0], np.cumsum(spec.q_lens)])
+    targets = []
+    for s_, n in enumerate(q_lens):
+        j = n // 2
+        kn[cu[s_] + j, :, 0] = 40.0
+        targets.append(j)
+    tens = wl.PassTensors(q=wl.bf16_round(q), k_new=wl.bf16_round(kn), v_new=base.v_new,
+                          hist_k=wl.bf16_round(np.zeros_like(base.hist_k, dtype=np.float32)), hist_v=base.hist_v)
+    _, _, _, out, lse, plan = G.full_gpu_pass(spec, tens=tens, mode="direct")
+    out = out.cpu().numpy()
+    g_ratio = hq // hkv
+    for s_, j_t in enumerate(targets):
+        want = _bits_to_f32(base.v_new[cu[s_] + j_t])            # [Hkv, D]
+        for j in range(j_t, q_lens[s_]):
+            for h in range(hq):
+                assert np.array_equal(out[cu[s_] + j, h], want[h // g_ratio]), (name, s_, j, h)
+
+
 def test_sequence_order_permutes_rows_bit_identically():
     # Shuffling the sequences of a pass permutes its output rows and changes
     # nothing else: same split structure per sequence, same arithmetic.
@@ -469,14 +545,18 @@ def test_workspace_too_small_is_rejected():
 
 # ---------------------------------------------------------------- full-size workloads
 
-@pytest.mark.parametrize("name", ["7b_pass2048", "70b_share4096"])
-def test_full_size_mixed_pass_all_rows(name):
+@pytest.mark.parametrize("name,mode", [("7b_pass2048", "separate"), ("70b_share4096", "separate"),
+                                       ("7b_pass2048", "pass"), ("70b_share4096", "pass")])
+def test_full_size_mixed_pass_all_rows(name, mode):
     spec = wl.config_spec(name)
-    _log(f"[case] full {name} S={spec.num_seqs} T={spec.num_tokens}")
-    tens, _, _, out, lse, plan = G.full_gpu_pass(spec)
+    _log(f"[case] full {name} ({mode}) S={spec.num_seqs} T={spec.num_tokens}")
+    tens, kp, vp, out, lse, plan = G.full_gpu_pass(spec, mode=mode)
     _log(f"[plan] {plan.info}")
     o_ref, l_ref = G.oracle_pass(spec, tens)
-    compare(out, lse, o_ref, l_ref, name)
+    compare(out, lse, o_ref, l_ref, f"{name} ({mode})")
+    if mode == "pass":
+        kref, vref = oracle_pools(spec, tens, poison=True)
+        assert np.array_equal(G.to_host_bits(kp), kref) and np.array_equal(G.to_host_bits(vp), vref)
 
 
 def test_full_size_decode64_every_row():
