@@ -272,7 +272,7 @@ def trace_cpu_baseline(passes, hq, hkv, d, bs, seed, wl, n_sample=8):
 
 
 def replay_trace(torch, fgb, wl, reqs, clients, policy, warmup=1, trace_passes=0, separate=False,
-                 record_kernels=True):
+                 record_kernels=True, api="pass"):
     """Replay a request trace through the host scheduler at `clients` closed-loop
     clients under composition `policy`.
 
@@ -325,28 +325,67 @@ def replay_trace(torch, fgb, wl, reqs, clients, policy, warmup=1, trace_passes=0
     lse = torch.empty((t_max, hq), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
-    def replay(record):
+    # Gated replays: the per-pass events must time device work only, but at
+    # few clients a pass takes less device time than its host-side planning
+    # and launch, so the device would idle between passes and the idle time
+    # would land inside the events.  Before each chunk of 6 passes (fewer
+    # than the library's pinned upload slots, so the host never waits for one
+    # while the device sleeps) a bounded spin kernel (torch.cuda._sleep) holds
+    # the stream for twice the wall time six passes took in the ungated
+    # replay, plus 0.3 ms, so the whole chunk is queued before the device
+    # reaches it and its passes run back to back.
+    gate_chunk = 6   # fewer passes than the library's 8 pinned upload slots: the host never
+                     # waits for a slot while the device sleeps
+    # the spin kernel's counter rate, measured once (cycles per second)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(1000)
+    e0.record(stream)
+    torch.cuda._sleep(2_000_000)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    gate_rate = 2_000_000 / max(1e-6, e0.elapsed_time(e1) * 1e-3)
+    gate_cycles = [0]
+
+    # per-pass events, created (and recorded once, which creates the HIP
+    # event) before any timed replay: event creation inside a replay can stall
+    # the host for milliseconds when the runtime grows its event pool
+    pass_events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in passes]
+    for e0, e1 in pass_events:
+        e0.record(stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+
+    def replay(record, gated=False):
         keep, evs, host = [], [], []
-        for p, (q, k, v) in zip(passes, inputs):
+        for i, (p, (q, k, v)) in enumerate(zip(passes, inputs)):
+            if gated and i % gate_chunk == 0:
+                torch.cuda._sleep(gate_cycles[0])
             h0 = time.perf_counter()
             plan = fgb.Plan(p.q_lens, p.ctx_lens, p.block_tables, hq, hkv, d, bs, nb)
             host.append(time.perf_counter() - h0)
             t = p.num_tokens
             if record:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0, e1 = pass_events[i]
                 e0.record(stream)
-            if separate:
-                plan.upload(meta, stream)
-                fgb.kv_append(plan, meta, k, v, kp, vp, stream)
+            if api == "pass":
+                fgb.run_pass(plan, meta, q, k, v, kp, vp, out[:t], lse[:t], workspace=ws, stream=stream)
             else:
-                fgb.upload_append(plan, meta, k, v, kp, vp, stream)
-            fgb.attention_ragged(plan, meta, q, kp, vp, out[:t], lse[:t], workspace=ws, stream=stream)
+                if separate:
+                    plan.upload(meta, stream)
+                    fgb.kv_append(plan, meta, k, v, kp, vp, stream)
+                else:
+                    fgb.upload_append(plan, meta, k, v, kp, vp, stream)
+                fgb.attention_ragged(plan, meta, q, kp, vp, out[:t], lse[:t], workspace=ws, stream=stream)
             if record:
                 e1.record(stream)
                 evs.append((e0, e1))
             keep.append(plan)
         return keep, evs, host
 
+    import gc
+    gc.collect()
+    gc.disable()   # a collection pause inside a gated chunk would land in its events
     for _ in range(max(0, warmup)):
         replay(False)
         torch.cuda.synchronize()
@@ -360,13 +399,23 @@ def replay_trace(torch, fgb, wl, reqs, clients, policy, warmup=1, trace_passes=0
     wall = time.perf_counter() - t0
     fgb.fg_profile_enable(False)
     kern = fgb.fg_profile_read()
+    per_ungated = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    keep.clear()
+    # the device timeline: per-pass device times from a gated replay; each
+    # gate lasts twice the ungated replay's wall time for a chunk, plus 0.3 ms
+    gate_cycles[0] = int(gate_rate * min(0.2, 0.0003 + 2.0 * gate_chunk * wall / len(passes)))
+    print(json.dumps({"replay": f"{policy} x{clients}", "passes": len(passes), "wall_s": round(wall, 2),
+                      "gate_rate_hz": round(gate_rate)}), file=sys.stderr, flush=True)
+    keep, evs, _ = replay(True, gated=True)
+    torch.cuda.synchronize()
     per = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
     keep.clear()
+    gc.enable()
     del inputs, big, kp, vp
     torch.cuda.empty_cache()
     return {"passes": passes, "full_passes": full_passes, "arrivals": arrivals, "pool_blocks": nb,
-            "per_us": per, "wall_s": wall, "host_s": host, "kern": kern, "t_max": t_max,
-            "shape": (hq, hkv, d, bs, seed)}
+            "per_us": per, "per_us_ungated": per_ungated, "wall_s": wall, "host_s": host, "kern": kern,
+            "t_max": t_max, "shape": (hq, hkv, d, bs, seed)}
 
 
 def full_budget_ref_us(passes, per_us, budget=2048):
@@ -381,7 +430,7 @@ def run_trace(args, torch, fgb, wl):
 
     reqs = sf.trace_requests()
     r = replay_trace(torch, fgb, wl, reqs, args.clients, args.serve_policy, warmup=args.warmup,
-                     trace_passes=args.trace_passes, separate=args.separate_append)
+                     trace_passes=args.trace_passes, separate=args.separate_append, api=args.api)
     passes, per, wall, kern = r["passes"], r["per_us"], r["wall_s"], r["kern"]
     hq, hkv, d, bs, seed = r["shape"]
     serving = None
@@ -411,6 +460,8 @@ def run_trace(args, torch, fgb, wl):
             "pass_device_us": {q: round(float(np.percentile(per, v)), 2)
                                for q, v in (("p10", 10), ("p50", 50), ("p90", 90), ("p99", 99), ("max", 100))},
             "device_total_ms": round(float(per.sum()) / 1e3, 3),
+            "device_timeline": "per-pass HIP events of a second, gated replay (each chunk of 6 passes "
+                               "queued behind a bounded spin, so passes run back to back)",
             "host_plan_us_median": round(float(np.median(r["host_s"])) * 1e6, 1),
             "kernel_ms_total": {k: round(v[0], 3) for k, v in kern.items()},
             "attn_gbs_avg": round(kv_bytes / (attn_ms * 1e-3) / 1e9, 1) if attn_ms else None,
@@ -441,7 +492,7 @@ def run_serve_sweep(args, torch, fgb, wl):
     order = [(c, pol) for c in sorted(SERVE_CLIENTS, reverse=True) for pol in sf.POLICIES]
     for i, (clients, pol) in enumerate(order):
         r = replay_trace(torch, fgb, wl, reqs, clients, pol, warmup=1 if i == 0 else 0,
-                         separate=args.separate_append, record_kernels=False)
+                         separate=args.separate_append, record_kernels=False, api=args.api)
         runs[(clients, pol)] = r
         print(json.dumps({"clients": clients, "policy": pol, "passes": len(r["passes"]),
                           "device_ms": round(float(r["per_us"].sum()) / 1e3, 2)}), file=sys.stderr, flush=True)
