@@ -854,7 +854,7 @@ def main():
             "attn_mfma_frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
             "floor_us": {"hbm": round(hbm_floor_us, 2), "mfma": round(mfma_floor_us, 2)},
             "pass_roofline_frac": round(max(hbm_floor_us, mfma_floor_us) / pass_us, 4),
-            "append_gbs": round(alg["append_bytes"] / (app_us * 1e-6) / 1e9, 1),
+            "append_gbs": round(alg["append_bytes"] / (app_us * 1e-6) / 1e9, 1) if app_us > 0 else None,
             "host_plan_us_median": round(float(np.median(host_plan_s)) * 1e6, 1) if host_plan_s else None,
             "warm_pass_device_us": {"p10": round(float(np.percentile(warm, 10)), 2),
                                     "median": round(float(np.median(warm)), 2),
