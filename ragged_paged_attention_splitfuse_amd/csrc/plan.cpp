@@ -120,36 +120,44 @@ struct Pending {
   int32_t order;
 };
 
-// The first launch rounds are resident together: the matrix-core kernel
-// holds kMfmaSlotsPerCu work-groups per CU, and MI355X's dispatcher hands
+// Work-groups one CU holds at once for the kernel a plan runs: the
+// matrix-core kernel's register budget allows kMfmaSlotsPerCu; the decode-only
+// kernel (no matrix-core items) uses 158-162 VGPRs at D = 128 (three
+// wavefronts per SIMD) and fewer than 128 at D = 64 (four).  Only the dispatch
+// order depends on these.
+constexpr int kValuSlotsPerCuD128 = 3;
+constexpr int kValuSlotsPerCuD64 = 4;
+
+// The first launch rounds are resident together: MI355X's dispatcher hands
 // work-group p of a fresh launch to CU (p mod C) in round p / C (it deals
 // them round-robin over the XCDs and, within each, one per CU before a
-// second).  Two work-groups on one CU share its matrix cores, so the CU
-// finishes with the sum of their costs.  Longest-first order would pair the
-// longest item with the (C+1)-th longest; instead the first C * kMfmaSlotsPerCu
-// items are dealt costliest-first onto the least-loaded CU with a free slot
-// (greedy multiway partition) and written back at positions cu + round * C,
-// CUs holding fewer items last.  Items after those rounds keep their order
-// and fill whichever CU frees a slot first.  Only speed depends on this.
-void place_resident_rounds(std::vector<Pending>& list, int cus) {
-  static_assert(kMfmaSlotsPerCu == 2, "CU bins hold two items");
+// second; per-work-group HW_ID readings showed positions p, p + C and p + 2C on
+// one CU for every position).  Work-groups on one CU share its matrix cores,
+// and a CU of the decode-only kernel streams about the same total (28-29 GB/s
+// at full load) whether it holds two or three work-groups, so a CU finishes
+// roughly with the sum of its items' costs.  Longest-first order would put
+// the longest item of every round on the same CUs; instead the first
+// C * slots items are dealt costliest-first onto the least-loaded CU with a
+// free slot (greedy multiway partition) and written back at positions
+// cu + round * C, CUs holding more items first.  Items after those rounds
+// keep their order and fill whichever CU frees a slot first.  Only speed
+// depends on this.
+void place_resident_rounds(std::vector<Pending>& list, int cus, int slots) {
   const size_t c = size_t(cus);
-  const size_t m = std::min(list.size(), c * kMfmaSlotsPerCu);
+  const size_t m = std::min(list.size(), c * size_t(slots));
   if (m <= c) return;
   std::vector<uint32_t> idx(m);
   std::iota(idx.begin(), idx.end(), 0u);
   std::stable_sort(idx.begin(), idx.end(),
                    [&](uint32_t x, uint32_t y) { return list[x].cost > list[y].cost; });
   // The costliest c items open one bin each; the rest go, costliest first,
-  // to the least-loaded bin still holding one item (ties: lower bin).
-  std::vector<double> load(c);
-  std::vector<uint32_t> first(c), second(c, UINT32_MAX);
+  // to the least-loaded bin with a free slot (ties: lower bin).
+  std::vector<std::vector<uint32_t>> bin(c);
   using Entry = std::pair<double, uint32_t>;
   std::vector<Entry> heap(c);
   for (size_t u = 0; u < c; ++u) {
-    first[u] = idx[u];
-    load[u] = list[idx[u]].cost;
-    heap[u] = {load[u], uint32_t(u)};
+    bin[u].push_back(idx[u]);
+    heap[u] = {list[idx[u]].cost, uint32_t(u)};
   }
   auto cmp = [](const Entry& x, const Entry& y) {
     return x.first != y.first ? x.first > y.first : x.second > y.second;
@@ -157,23 +165,26 @@ void place_resident_rounds(std::vector<Pending>& list, int cus) {
   std::make_heap(heap.begin(), heap.end(), cmp);
   for (size_t i = c; i < m; ++i) {
     std::pop_heap(heap.begin(), heap.end(), cmp);
-    const uint32_t u = heap.back().second;
+    Entry e = heap.back();
     heap.pop_back();
-    second[u] = idx[i];
+    bin[e.second].push_back(idx[i]);
+    if (bin[e.second].size() < size_t(slots)) {
+      heap.push_back({e.first + list[idx[i]].cost, e.second});
+      std::push_heap(heap.begin(), heap.end(), cmp);
+    }
   }
-  // Bins holding two items first: round 0 takes every bin's first item, round
-  // 1 the second items, so bin u's pair sits at positions u and u + c.
+  // Round r takes the r-th item of every bin holding more than r items; bins
+  // are ordered by item count (then bin index), so those bins come first in
+  // every round and bin u's items sit at positions u, u + c, ...
   std::vector<uint32_t> order(c);
-  size_t lo = 0, hi = c;
-  for (size_t u = 0; u < c; ++u) {
-    if (second[u] != UINT32_MAX) order[lo++] = uint32_t(u);
-    else order[--hi] = uint32_t(u);
-  }
-  std::reverse(order.begin() + lo, order.end());   // keep single bins in bin order
+  std::iota(order.begin(), order.end(), 0u);
+  std::stable_sort(order.begin(), order.end(),
+                   [&](uint32_t x, uint32_t y) { return bin[x].size() > bin[y].size(); });
   std::vector<Pending> placed;
   placed.reserve(m);
-  for (size_t k = 0; k < c; ++k) placed.push_back(list[first[order[k]]]);
-  for (size_t k = 0; k < lo; ++k) placed.push_back(list[second[order[k]]]);
+  for (int r = 0; r < slots; ++r)
+    for (size_t k = 0; k < c && bin[order[k]].size() > size_t(r); ++k)
+      placed.push_back(list[bin[order[k]][size_t(r)]]);
   std::copy(placed.begin(), placed.end(), list.begin());
 }
 
@@ -531,7 +542,9 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
                             (a < mfma.size() && (double(a) + 0.5) / na <= (double(b) + 0.5) / nb);
         order_list.push_back(take_a ? mfma[a++] : valu[b++]);
       }
-      if (!mfma.empty()) place_resident_rounds(order_list, target_cus);
+      const int slots = !mfma.empty() ? kMfmaSlotsPerCu
+                        : (D == 64 ? kValuSlotsPerCuD64 : kValuSlotsPerCuD128);
+      place_resident_rounds(order_list, target_cus, slots);
       for (size_t o = 0; o < order_list.size(); ++o) items[o] = order_list[o].item;
     }
     if (!merges.empty())

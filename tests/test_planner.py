@@ -114,8 +114,10 @@ def test_items_are_longest_first_per_kind_and_interleaved():
     for name in ("7b_decode64", "7b_pass2048", "70b_share4096"):
         items = plan_of(wl.config_spec(name)).metadata()["items"]
         cost, mf = _item_costs(items)
-        # with tiles present, the two resident rounds are reordered for balance
-        m = min(len(items), 2 * CUS) if mf.any() else 0
+        # the resident rounds are reordered for balance: two work-groups per
+        # CU in the kernel with matrix-core items, three in the decode-only
+        # kernel at D = 128
+        m = min(len(items), (2 if mf.any() else 3) * CUS)
         cost, mf = cost[m:], mf[m:]
         assert np.all(np.diff(cost[mf]) <= 1e-9) and np.all(np.diff(cost[~mf]) <= 0)
         if mf.any() and (~mf).any():
@@ -138,6 +140,28 @@ def test_resident_rounds_balance_cu_pairs(name):
     assert loads.max() <= naive.max() + 1e-9
     assert loads.max() - loads.min() <= cost[:m].max() + 1e-9
     if name in ("7b_chunk2032", "70b_chunks"):
+        assert loads.max() <= 1.01 * loads.mean()
+
+
+@pytest.mark.parametrize("name", ["7b_decode16", "7b_decode64"])
+def test_resident_rounds_balance_three_slots_in_decode_only_plans(name):
+    # decode-only plans at D = 128 run three work-groups per CU: positions p,
+    # p + CUS and p + 2 CUS share a CU, and their summed cost is evened out
+    items = plan_of(wl.config_spec(name)).metadata()["items"]
+    cost, mf = _item_costs(items)
+    assert not mf.any()
+    m = min(len(items), 3 * CUS)
+    loads = np.zeros(CUS)
+    for pos in range(m):
+        loads[pos % CUS] += cost[pos]
+    top = np.sort(cost[:m])[::-1]            # plain longest-first dealing
+    naive = np.zeros(CUS)
+    for pos in range(m):
+        naive[pos % CUS] += top[pos]
+    assert loads.max() <= naive.max() + 1e-9
+    assert loads.max() - loads.min() <= 2 * cost[:m].max() + 1e-9
+    assert loads.max() <= 1.06 * loads.mean()
+    if m == 3 * CUS:
         assert loads.max() <= 1.01 * loads.mean()
 
 
