@@ -39,7 +39,8 @@ class fg_pass_desc(ctypes.Structure):
         ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
         ("max_blocks_per_seq", ctypes.c_int32), ("scale", ctypes.c_float),
-        ("q_lens", _I32P), ("ctx_lens", _I32P), ("block_tables", _I32P),
+        # const int32_t* in the header; set from array addresses (plain ints)
+        ("q_lens", ctypes.c_void_p), ("ctx_lens", ctypes.c_void_p), ("block_tables", ctypes.c_void_p),
         ("target_cus", ctypes.c_int32), ("min_split_tokens", ctypes.c_int32),
         ("max_splits", ctypes.c_int32), ("force_splits", ctypes.c_int32),
         ("split_policy", ctypes.c_int32),
@@ -168,9 +169,9 @@ class Plan:
         d.block_size, d.num_blocks = block_size, num_blocks
         d.max_blocks_per_seq = bt.shape[1] if bt.ndim == 2 else 0
         d.scale = float(scale)
-        d.q_lens = q.ctypes.data_as(_I32P)
-        d.ctx_lens = c.ctypes.data_as(_I32P)
-        d.block_tables = bt.ctypes.data_as(_I32P)
+        d.q_lens = q.__array_interface__["data"][0]
+        d.ctx_lens = c.__array_interface__["data"][0]
+        d.block_tables = bt.__array_interface__["data"][0]
         d.target_cus, d.min_split_tokens = target_cus, min_split_tokens
         d.max_splits, d.force_splits = max_splits, force_splits
         d.split_policy = split_policy

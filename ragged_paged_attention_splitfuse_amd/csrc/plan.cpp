@@ -143,21 +143,25 @@ constexpr int kValuSlotsPerCuD64 = 4;
 // keep their order and fill whichever CU frees a slot first.  Only speed
 // depends on this.
 void place_resident_rounds(std::vector<Pending>& list, int cus, int slots) {
-  const size_t c = size_t(cus);
-  const size_t m = std::min(list.size(), c * size_t(slots));
+  const size_t c = size_t(cus), k = size_t(slots);
+  const size_t m = std::min(list.size(), c * k);
   if (m <= c) return;
+  std::vector<double> cost(m);
+  for (size_t i = 0; i < m; ++i) cost[i] = list[i].cost;
   std::vector<uint32_t> idx(m);
   std::iota(idx.begin(), idx.end(), 0u);
-  std::stable_sort(idx.begin(), idx.end(),
-                   [&](uint32_t x, uint32_t y) { return list[x].cost > list[y].cost; });
+  std::sort(idx.begin(), idx.end(),
+            [&](uint32_t x, uint32_t y) { return cost[x] != cost[y] ? cost[x] > cost[y] : x < y; });
   // The costliest c items open one bin each; the rest go, costliest first,
-  // to the least-loaded bin with a free slot (ties: lower bin).
-  std::vector<std::vector<uint32_t>> bin(c);
+  // to the least-loaded bin with a free slot (ties: lower bin).  Bin u's
+  // items are bin_item[u * k .. u * k + count[u]).
+  std::vector<uint32_t> bin_item(c * k);
+  std::vector<uint32_t> count(c, 1);
   using Entry = std::pair<double, uint32_t>;
   std::vector<Entry> heap(c);
   for (size_t u = 0; u < c; ++u) {
-    bin[u].push_back(idx[u]);
-    heap[u] = {list[idx[u]].cost, uint32_t(u)};
+    bin_item[u * k] = idx[u];
+    heap[u] = {cost[idx[u]], uint32_t(u)};
   }
   auto cmp = [](const Entry& x, const Entry& y) {
     return x.first != y.first ? x.first > y.first : x.second > y.second;
@@ -165,26 +169,27 @@ void place_resident_rounds(std::vector<Pending>& list, int cus, int slots) {
   std::make_heap(heap.begin(), heap.end(), cmp);
   for (size_t i = c; i < m; ++i) {
     std::pop_heap(heap.begin(), heap.end(), cmp);
-    Entry e = heap.back();
+    const Entry e = heap.back();
     heap.pop_back();
-    bin[e.second].push_back(idx[i]);
-    if (bin[e.second].size() < size_t(slots)) {
-      heap.push_back({e.first + list[idx[i]].cost, e.second});
+    const uint32_t u = e.second;
+    bin_item[u * k + count[u]++] = idx[i];
+    if (count[u] < k) {
+      heap.push_back({e.first + cost[idx[i]], u});
       std::push_heap(heap.begin(), heap.end(), cmp);
     }
   }
   // Round r takes the r-th item of every bin holding more than r items; bins
   // are ordered by item count (then bin index), so those bins come first in
   // every round and bin u's items sit at positions u, u + c, ...
-  std::vector<uint32_t> order(c);
-  std::iota(order.begin(), order.end(), 0u);
-  std::stable_sort(order.begin(), order.end(),
-                   [&](uint32_t x, uint32_t y) { return bin[x].size() > bin[y].size(); });
+  std::vector<uint32_t> order;
+  order.reserve(c);
+  for (size_t n = k; n >= 1; --n)
+    for (size_t u = 0; u < c; ++u)
+      if (count[u] == n) order.push_back(uint32_t(u));
   std::vector<Pending> placed;
   placed.reserve(m);
-  for (int r = 0; r < slots; ++r)
-    for (size_t k = 0; k < c && bin[order[k]].size() > size_t(r); ++k)
-      placed.push_back(list[bin[order[k]][size_t(r)]]);
+  for (size_t r = 0; r < k; ++r)
+    for (size_t j = 0; j < c && count[order[j]] > r; ++j) placed.push_back(list[bin_item[order[j] * k + r]]);
   std::copy(placed.begin(), placed.end(), list.begin());
 }
 
@@ -366,8 +371,6 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
             ? 1e300
             : std::max(1.0, tile_cost / (double(target_cus) * kMfmaSlotsPerCu));
     std::vector<Pending> mfma, valu;
-    mfma.reserve(groups.size());
-    valu.reserve(groups.size() * 2);
     std::vector<MergeRec> merges, late_merges;
     int64_t partial_rows = 0;
     int max_used = 1;
@@ -418,6 +421,13 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
     }
     const bool inlaunch_ok =
         total_items <= int64_t(kInLaunchMaxItemsPerSlot) * target_cus * kMfmaSlotsPerCu;
+    {
+      int64_t n_mfma_items = 0;
+      for (size_t gi = 0; gi < groups.size(); ++gi)
+        if (groups[gi].waves) n_mfma_items += gk[gi];
+      mfma.reserve(size_t(n_mfma_items));
+      valu.reserve(size_t(total_items - n_mfma_items));
+    }
     for (size_t gi = 0; gi < groups.size(); ++gi) {
       const Group& grp = groups[gi];
       const int64_t k = gk[gi], chunk = gchunk[gi];
