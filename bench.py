@@ -444,6 +444,16 @@ def run_trace(args, torch, fgb, wl):
                                         + p.q_lens.astype(np.int64) * (p.q_lens + 1) // 2))
                 for p in passes)
     attn_ms, attn_n = kern["attn_kernel"]
+    # Roofline of the attention launches over the whole replay: algorithmic
+    # bytes (KV + Q + fp32 O + LSE of every pass) over their summed event time.
+    # HBM-bound like the 7B pass; no counter runs cover the trace (traffic null).
+    roof = None
+    if attn_ms and attn_n == len(passes):
+        attn_bytes = kv_bytes + sum(p.num_tokens * hq * (d * (2 + 4) + 4) for p in passes)
+        gbs = attn_bytes / (attn_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "kernel": "attn_kernel",
+                "algorithmic_per_launch": int(attn_bytes // attn_n), "launches": attn_n}
     res = {
         "metric": METRIC, "value": round(wall * 1e6 / len(passes), 2), "unit": "µs",
         "n_gpus": 1, "steps": len(passes), "warmup": args.warmup,
@@ -453,7 +463,7 @@ def run_trace(args, torch, fgb, wl):
                    "clients": args.clients, "budget": 2048, "max_pass_tokens": r["t_max"],
                    "q_heads": hq, "kv_heads": hkv, "head_dim": d, "block_size": bs,
                    "passes": len(passes), "trace_passes": r["full_passes"], "pool_blocks": r["pool_blocks"]},
-        "roofline": None, "cpu_baseline": None,
+        "roofline": roof, "cpu_baseline": None,
         "detail": {
             "total_ms": round(wall * 1e3, 3), "tokens": toks,
             "tokens_per_s": round(toks / wall, 1),
