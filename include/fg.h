@@ -244,12 +244,15 @@ fg_status fg_attention_ragged_direct(const fg_plan* plan, void* d_meta, const vo
                                      void* stream);
 
 /* One whole pass: the plan's metadata upload, the KV append and the attention
- * (plus the merge launch when the plan splits prefill tiles), with the append
- * done by work-groups of the attention launch.  Attention reads key positions
- * below each sequence's cached context from the pools and the pass's own
- * positions straight from k_new / v_new, so it does not wait for the append;
- * the pools hold the pass's K/V once the stream has passed the call, bit for
- * bit as fg_kv_append writes them ("DeepSpeed-FastGen Guide: Dynamic SplitKV
+ * (plus the merge launch when the plan splits prefill tiles).  For a plan
+ * without prefill tiles the append is done by work-groups of the attention
+ * launch, and attention reads key positions below each sequence's cached
+ * context from the pools and the pass's own positions straight from k_new /
+ * v_new, so it does not wait for the append.  A plan with prefill tiles runs
+ * the fused upload + append launch first and then the attention launch over
+ * the pools (tiles staged from the pools measured faster).  Either way the
+ * pools hold the pass's K/V once the stream has passed the call, bit for bit
+ * as fg_kv_append writes them ("DeepSpeed-FastGen Guide: Dynamic SplitKV
  * Serving", section "3. Paged KV Memory Management with Zero Overhead": the
  * kernel reads the block tables itself, with no separate translation pass).
  * Arguments as for fg_plan_upload, fg_kv_append and fg_attention_ragged
