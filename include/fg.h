@@ -25,6 +25,8 @@
  *     ... stream sync ... -> fg_plan_destroy
  * or, with the first two device steps in one launch,
  *     fg_plan_pass -> fg_upload_append -> fg_attention_ragged -> ...
+ * or the whole pass in one call,
+ *     fg_plan_pass -> fg_pass -> ... stream sync ... -> fg_plan_destroy
  *
  * Conventions
  * -----------
@@ -32,8 +34,10 @@
  *   exception crosses the ABI and nothing aborts.
  * - All validation happens in fg_plan_pass; a plan that exists is valid, and
  *   the kernels never see an index outside the pools.
- * - The library never allocates device memory.  The caller owns every device
- *   buffer (metadata, workspace, pools, inputs, outputs) and the stream.
+ * - The library calls no device allocator.  The caller owns every device
+ *   buffer (metadata, workspace, pools, inputs, outputs) and the stream; the
+ *   library's only device memory of its own is the static scratch array behind
+ *   fg_attention_ragged_noalloc.
  * - Device pointers must be 16-byte aligned.  `stream` is a hipStream_t passed
  *   as void* (NULL = the null stream).
  * - Plans are immutable after fg_plan_pass; functions are reentrant.  Calls
@@ -317,6 +321,17 @@ typedef struct fg_plan_layout_t {
 
 fg_status fg_plan_metadata(const fg_plan* plan, void* host_dst, size_t bytes,
                            fg_plan_layout_t* layout);
+
+/* Work-groups one CU holds at once.  *planned: the count fg_plan_pass assumed
+ * when it dealt the plan's first launch rounds onto the CUs (the matrix-core
+ * kernel's for plans with matrix-core items, else the decode-only kernel's);
+ * it affects speed only.  *device: what the HIP occupancy calculator gives for
+ * the attention kernels this plan can launch on the current device (the
+ * smaller of the pool-reading and the direct instantiation), or -1 when it
+ * cannot be queried (no GPU).  Introspection for tests; no launch.
+ * FG_E_INVALID for a null argument, FG_E_UNSUPPORTED for an unsupported
+ * head_dim / block_size. */
+fg_status fg_plan_resident_slots(const fg_plan* plan, int32_t* planned, int32_t* device);
 
 /* ---- measurement hooks ------------------------------------------------------
  * fg_profile_enable(mask): bit (1 << FG_KERNEL_x) of mask makes the library

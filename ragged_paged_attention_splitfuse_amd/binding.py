@@ -93,6 +93,7 @@ SIGNATURES = {
     "fg_abi_version": (ctypes.c_int32, []),
     "fg_plan_metadata": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                           ctypes.POINTER(fg_plan_layout_t)]),
+    "fg_plan_resident_slots": (ctypes.c_int32, [ctypes.c_void_p, _I32P, _I32P]),
     "fg_profile_enable": (ctypes.c_int32, [ctypes.c_int32]),
     "fg_profile_read": (ctypes.c_int32, [ctypes.POINTER(ctypes.c_double), _I32P, ctypes.c_int32]),
     "fg_kernel_name": (ctypes.c_char_p, [ctypes.c_int32]),
@@ -223,6 +224,14 @@ class Plan:
             "counters": words[lay.counters // 4: lay.counters // 4 + lay.num_counters].copy(),
             "raw": buf[:nbytes].copy(),
         }
+
+    def resident_slots(self):
+        """(planned, device): work-groups per CU the planner assumed, and what the
+        occupancy calculator gives for this plan's attention kernels (-1 without a GPU)."""
+        planned, device = ctypes.c_int32(), ctypes.c_int32()
+        _check(lib().fg_plan_resident_slots(self.handle, ctypes.byref(planned), ctypes.byref(device)),
+               "fg_plan_resident_slots")
+        return planned.value, device.value
 
     def upload(self, d_meta=None, stream=None, device="cuda"):
         """fg_plan_upload into d_meta (allocated here as a torch uint8 tensor if None)."""

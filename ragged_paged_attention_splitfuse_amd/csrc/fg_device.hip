@@ -1559,6 +1559,36 @@ extern "C" fg_status fg_pass(const fg_plan* plan, void* d_meta, const void* q, c
                           static_cast<hipStream_t>(stream), true, k_new, v_new, true);
 }
 
+extern "C" fg_status fg_plan_resident_slots(const fg_plan* plan, int32_t* planned, int32_t* device) {
+  if (!plan || !planned || !device) return FG_E_INVALID;
+  *planned = plan->resident_slots;
+  *device = -1;
+  int pool = 0, direct = 0;
+  hipError_t e0 = hipSuccess, e1 = hipSuccess;
+#define FG_OCCUPANCY(D_, B_)                                                                       \
+  do {                                                                                             \
+    if (plan->n_mfma > 0) {                                                                        \
+      e0 = hipOccupancyMaxActiveBlocksPerMultiprocessor(&pool, attn_kernel<D_, B_, true, false>,   \
+                                                        kThreads, 0);                              \
+      e1 = hipOccupancyMaxActiveBlocksPerMultiprocessor(&direct, attn_kernel<D_, B_, true, true>,  \
+                                                        kThreads, 0);                              \
+    } else {                                                                                       \
+      e0 = hipOccupancyMaxActiveBlocksPerMultiprocessor(&pool, attn_kernel<D_, B_, false, false>,  \
+                                                        kThreads, 0);                              \
+      e1 = hipOccupancyMaxActiveBlocksPerMultiprocessor(&direct, attn_kernel<D_, B_, false, true>, \
+                                                        kThreads, 0);                              \
+    }                                                                                              \
+  } while (0)
+  FG_SWITCH_DB(plan->head_dim, plan->block_size, FG_OCCUPANCY);
+#undef FG_OCCUPANCY
+  if (e0 != hipSuccess || e1 != hipSuccess) {
+    (void)hipGetLastError();   // no device: leave *device at -1
+    return FG_OK;
+  }
+  *device = pool < direct ? pool : direct;
+  return FG_OK;
+}
+
 extern "C" fg_status fg_profile_enable(int32_t mask) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   g_prof_mask = static_cast<uint32_t>(mask);

@@ -120,13 +120,20 @@ struct Pending {
   int32_t order;
 };
 
-// Work-groups one CU holds at once for the kernel a plan runs: the
-// matrix-core kernel's register budget allows kMfmaSlotsPerCu; the decode-only
-// kernel (no matrix-core items) uses 158-162 VGPRs at D = 128 (three
-// wavefronts per SIMD) and fewer than 128 at D = 64 (four).  Only the dispatch
-// order depends on these.
-constexpr int kValuSlotsPerCuD128 = 3;
-constexpr int kValuSlotsPerCuD64 = 4;
+// Work-groups one CU holds at once for the attention kernel a plan launches,
+// from the compiled kernels' register counts (VGPRs per wavefront, allocated in
+// granules of 8 from 512 per SIMD lane; the LDS never binds first):
+//   with matrix-core items, D = 128:        223-240 VGPRs -> 2
+//                           D = 64, B = 64: 172-174       -> 2
+//                           D = 64, B < 64: 164-166       -> 3
+//   decode-only kernel,     D = 128:        153-164       -> 3
+//                           D = 64:         116-127       -> 4
+// Only the dispatch order depends on these; tests/test_gpu_occupancy.py checks
+// them against the HIP occupancy calculator for every (D, B, kernel) pair.
+int resident_slots_per_cu(bool mfma, int D, int B) {
+  if (mfma) return (D == 64 && B < 64) ? 3 : kMfmaSlotsPerCu;
+  return D == 64 ? 4 : 3;
+}
 
 // The first launch rounds are resident together: MI355X's dispatcher hands
 // work-group p of a fresh launch to CU (p mod C) in round p / C (it deals
@@ -552,8 +559,8 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
                             (a < mfma.size() && (double(a) + 0.5) / na <= (double(b) + 0.5) / nb);
         order_list.push_back(take_a ? mfma[a++] : valu[b++]);
       }
-      const int slots = !mfma.empty() ? kMfmaSlotsPerCu
-                        : (D == 64 ? kValuSlotsPerCuD64 : kValuSlotsPerCuD128);
+      const int slots = resident_slots_per_cu(!mfma.empty(), D, B);
+      plan->resident_slots = slots;
       place_resident_rounds(order_list, target_cus, slots);
       for (size_t o = 0; o < order_list.size(); ++o) items[o] = order_list[o].item;
     }

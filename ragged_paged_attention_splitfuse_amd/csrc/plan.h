@@ -32,6 +32,7 @@ struct fg_plan {
   int32_t n_partial_rows = 0;
   int32_t max_splits_used = 0;
   int32_t target_cus = 0;
+  int32_t resident_slots = 0;   // work-groups per CU the dispatch order assumed
 
   // Workspace: partial O rows [n_partial_rows, D] fp32 then lse [n_partial_rows].
   size_t ws_o_off = 0, ws_lse_off = 0, ws_bytes = 0;

@@ -165,6 +165,26 @@ def test_resident_rounds_balance_three_slots_in_decode_only_plans(name):
         assert loads.max() <= 1.01 * loads.mean()
 
 
+def test_planned_resident_slots():
+    # work-groups per CU of the attention kernel a plan launches (from its
+    # register count): two with matrix-core items at D = 128 or B = 64, three at
+    # D = 64 with B < 64; three (D = 128) or four (D = 64) in the decode-only
+    # kernel.  No GPU here, so the device count reads -1 (the GPU test compares).
+    want = {(64, 16, True): 3, (64, 32, True): 3, (64, 64, True): 2,
+            (128, 16, True): 2, (128, 32, True): 2, (128, 64, True): 2,
+            (64, 16, False): 4, (64, 32, False): 4, (64, 64, False): 4,
+            (128, 16, False): 3, (128, 32, False): 3, (128, 64, False): 3}
+    for (d, b, tiles), n in want.items():
+        if tiles:
+            spec = wl.custom_spec("t", [1] * 8 + [300], [3000] * 8 + [500], 8, 8, d, b, seed=1)
+        else:
+            spec = wl.custom_spec("d", [1] * 40, [3000] * 40, 8, 8, d, b, seed=2)
+        plan = plan_of(spec)
+        assert (plan.info["num_mfma_items"] > 0) == tiles
+        planned, device = plan.resident_slots()
+        assert planned == n and device in (-1, n), (d, b, tiles)
+
+
 def test_tiny_plan_has_no_splits_and_no_workspace():
     plan = plan_of(wl.config_spec(1))
     assert plan.info["num_merge_groups"] == 0 and plan.info["workspace_bytes"] == 0
