@@ -60,8 +60,9 @@ def source_hash():
 def achievable_peaks(torch, fgb, dev, stream, copy_mib=1024, read_mib=2048, gemm_n=8192, iters=10):
     """Achievable rates measured in the same run: a device-to-device copy (HBM
     read + write), the library's read-stream probe over 2 GiB (eight times the
-    MALL; attention traffic is almost all reads), and a bf16 GEMM through the
-    vendor BLAS (matrix cores).  `hbm_gbs` is the larger of the two HBM rates."""
+    MALL; attention traffic is almost all reads), a bf16 GEMM through the vendor
+    BLAS and the library's matrix-core loop (with the shader clock it ran at).
+    `hbm_gbs` is the larger of the two HBM rates."""
     def timed(fn):
         for _ in range(2):
             fn()
@@ -88,12 +89,24 @@ def achievable_peaks(torch, fgb, dev, stream, copy_mib=1024, read_mib=2048, gemm
     b = torch.randn((gemm_n, gemm_n), dtype=torch.bfloat16, device=dev, generator=g)
     t_gemm = timed(lambda: torch.mm(a, b))
     del a, b
+    # the library's matrix-core loop: two work-groups per CU, 32 bf16 MFMAs per
+    # wavefront per round; its per-work-group counters give the shader clock
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    loop_iters = 1024
+    lsink = torch.empty(cus * 2 * 256, dtype=torch.float32, device=dev)
+    lclk = torch.zeros(cus * 2 * 2, dtype=torch.int64, device=dev)
+    t_loop = timed(lambda: fgb.fg_probe_mfma_loop(loop_iters, lsink, lclk, stream))
+    clk = lclk.view(-1, 2).cpu().numpy().astype(np.float64)
+    loop_flops = cus * 2 * 4 * loop_iters * 32 * 32 * 32 * 16 * 2
+    del lsink, lclk
     copy_gbs = round(2 * n / t_copy / 1e9, 1)
     read_gbs = round(nr / t_read / 1e9, 1)
     return {"copy_gbs": copy_gbs, "read_gbs": read_gbs, "hbm_gbs": max(copy_gbs, read_gbs),
             "copy_bytes": n, "read_bytes": nr,
             "bf16_gemm_tflops": round(2 * gemm_n ** 3 / t_gemm / 1e12, 1),
-            "gemm_shape": [gemm_n, gemm_n, gemm_n]}
+            "gemm_shape": [gemm_n, gemm_n, gemm_n],
+            "bf16_mfma_loop_tflops": round(loop_flops / t_loop / 1e12, 1),
+            "mfma_loop_clock_ghz": round(float(np.median(clk[:, 0] / (clk[:, 1] / 100e6))) / 1e9, 3)}
 
 
 def _pmc_per_dispatch(run_dir, counter):
@@ -895,7 +908,8 @@ def main():
             "achievable": achievable,
             "attn_frac_of_achievable": {
                 "hbm": round(attn_gbs / achievable["hbm_gbs"], 4),
-                "mfma": round(attn_tflops / achievable["bf16_gemm_tflops"], 4)} if achievable else None,
+                "mfma": round(attn_tflops / achievable["bf16_gemm_tflops"], 4),
+                "mfma_loop": round(attn_tflops / achievable["bf16_mfma_loop_tflops"], 4)} if achievable else None,
             "kernel_source_sha256_16": source_hash(),
             "kernel_events": args.kernel_events,
         },

@@ -363,6 +363,20 @@ const char* fg_kernel_name(int32_t kernel_id);
 fg_status fg_probe_read_stream(const void* buf, size_t bytes, void* sink, size_t sink_bytes,
                                void* stream);
 
+/* Achievable matrix-core rate and the shader clock under matrix-core load, for
+ * measurement only: one launch on `stream` of two 256-thread work-groups per
+ * compute unit, each wavefront issuing iters (1..2048) rounds of 32 bf16
+ * 32x32x16 MFMAs (32,768 flops each) on register operands.  Writes one float
+ * per thread into sink (>= 2 KiB per compute unit; each value is 8192 * iters)
+ * and, per work-group, two int64 counts into clocks (>= 32 bytes per compute
+ * unit): elapsed shader-clock cycles (s_memtime) and elapsed 100 MHz ticks
+ * (s_memrealtime).  Both buffers are caller-owned device memory.  Time it with
+ * events on the same stream.  FG_E_INVALID for null or misaligned pointers or
+ * iters out of range, FG_E_WORKSPACE for short buffers, FG_E_HIP if the launch
+ * fails. */
+fg_status fg_probe_mfma_loop(int32_t iters, void* sink, size_t sink_bytes, void* clocks,
+                             size_t clocks_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

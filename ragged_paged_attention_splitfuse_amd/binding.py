@@ -99,6 +99,8 @@ SIGNATURES = {
     "fg_kernel_name": (ctypes.c_char_p, [ctypes.c_int32]),
     "fg_probe_read_stream": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                               ctypes.c_size_t, ctypes.c_void_p]),
+    "fg_probe_mfma_loop": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
+                                            ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
 }
 
 
@@ -449,6 +451,14 @@ def fg_probe_read_stream(buf, sink, stream=None):
     _check(lib().fg_probe_read_stream(_ptr(buf), int(buf.numel() * buf.element_size()), _ptr(sink),
                                       int(sink.numel() * sink.element_size()), _stream(stream)),
            "fg_probe_read_stream")
+
+
+def fg_probe_mfma_loop(iters, sink, clocks, stream=None):
+    """One matrix-core loop launch (measurement only); `sink` holds >= 2 KiB and
+    `clocks` (int64) >= 32 bytes per CU."""
+    _check(lib().fg_probe_mfma_loop(int(iters), _ptr(sink), int(sink.numel() * sink.element_size()),
+                                    _ptr(clocks), int(clocks.numel() * clocks.element_size()),
+                                    _stream(stream)), "fg_probe_mfma_loop")
 
 
 # short aliases used by tests and bench

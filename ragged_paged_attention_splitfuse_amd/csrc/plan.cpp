@@ -187,7 +187,8 @@ void place_resident_rounds(std::vector<Pending>& list, int cus, int slots) {
   }
   // Round r takes the r-th item of every bin holding more than r items; bins
   // are ordered by item count (then bin index), so those bins come first in
-  // every round and bin u's items sit at positions u, u + c, ...
+  // every round and the j-th bin of that order has its items at positions j,
+  // j + c, j + 2c, ...
   std::vector<uint32_t> order;
   order.reserve(c);
   for (size_t n = k; n >= 1; --n)

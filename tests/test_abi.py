@@ -79,6 +79,17 @@ def test_read_stream_probe_rejects_bad_arguments_before_any_device_call():
     assert lib.fg_probe_read_stream(4104, 32, 8192, 1 << 20, None) == binding.FG_E_INVALID
 
 
+def test_mfma_loop_probe_rejects_bad_arguments_before_any_device_call():
+    lib = binding.lib()
+    # iteration count out of range, null or misaligned buffers: rejected
+    # before the pointers are used
+    assert lib.fg_probe_mfma_loop(0, 4096, 1 << 20, 8192, 1 << 20, None) == binding.FG_E_INVALID
+    assert lib.fg_probe_mfma_loop(4096, 4096, 1 << 20, 8192, 1 << 20, None) == binding.FG_E_INVALID
+    assert lib.fg_probe_mfma_loop(4, None, 1 << 20, 8192, 1 << 20, None) == binding.FG_E_INVALID
+    assert lib.fg_probe_mfma_loop(4, 4098, 1 << 20, 8192, 1 << 20, None) == binding.FG_E_INVALID
+    assert lib.fg_probe_mfma_loop(4, 4096, 1 << 20, 8196, 1 << 20, None) == binding.FG_E_INVALID
+
+
 def test_profile_mask_toggles_without_a_device():
     # Enabling, selecting kernels and reading an empty record make no device call.
     binding.fg_profile_enable(True, (binding.FG_KERNEL_ATTENTION,))

@@ -41,3 +41,30 @@ def test_read_stream_probe_rejects_a_short_sink():
     with pytest.raises(binding.FgError) as e:
         binding.fg_probe_read_stream(buf, sink)
     assert e.value.status == binding.FG_E_WORKSPACE
+
+
+def test_mfma_loop_probe_computes_exactly_and_reports_a_clock():
+    import torch
+    dev = torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    iters = 64
+    sink = torch.full((cus * 2 * 256,), -1.0, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(cus * 2 * 2, dtype=torch.int64, device=dev)
+    binding.fg_probe_mfma_loop(iters, sink, clocks)
+    torch.cuda.synchronize()
+    # all-ones operands: every accumulator element is 16 * 8 * iters
+    assert bool(torch.all(sink == 8192.0 * iters))
+    c = clocks.view(-1, 2).cpu().numpy().astype(np.float64)
+    assert (c > 0).all()
+    ghz = c[:, 0] / (c[:, 1] / 100e6) / 1e9
+    assert 0.5 < float(np.median(ghz)) < 3.0
+
+
+def test_mfma_loop_probe_rejects_short_buffers():
+    import torch
+    dev = torch.device("cuda:0")
+    sink = torch.zeros(16, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(16, dtype=torch.int64, device=dev)
+    with pytest.raises(binding.FgError) as e:
+        binding.fg_probe_mfma_loop(4, sink, clocks)
+    assert e.value.status == binding.FG_E_WORKSPACE
