@@ -77,13 +77,15 @@ constexpr double kMfmaMinCost = 0.5;
 constexpr int kMfmaMinSplitTokens = 1024;
 constexpr int kMfmaSlotsPerCu = 2;
 // Split groups merged inside the attention launch: at most one wavefront's
-// rows, in plans of at most this many items per work-group slot.  Every split
-// item of such a group ends with a store drain and a device-scope atomic
-// round trip before it can exit, so a slot pays that latency once per item it
-// runs.  Measured: 64 decodes split 16 ways (55 items per slot) took 1,218 us
-// per pass in-launch and 1,064 us with a merge launch; the 70B-class decode
-// half (about one item per slot, 64 groups split 8 ways) took 59.0 us
-// in-launch and 64.5 us with the merge launch.
+// rows, in plans of at most this many items per work-group slot (slots of the
+// kernel the plan launches).  Every split item of such a group ends with a
+// store drain and a device-scope atomic round trip before it can exit, so a
+// slot pays that latency once per item it runs.  Measured: 64 decodes split
+// 16 ways (55 items per slot) took 1,218 us per pass in-launch and 1,064 us
+// with a merge launch; the 70B-class decode half (about one item per slot, 64
+// groups split 8 ways) took 59.0 us in-launch and 64.5 us with the merge
+// launch; 64 decodes at the default split (2,336 items, three slots per CU)
+// took 715 us in-launch and 728 us with the merge launch.
 constexpr int kInLaunchMaxItemsPerSlot = 4;
 // Decode-only passes with several groups per slot (many sequences, lengths
 // spread widely): the longest groups are each about one slot's share, and the
@@ -428,7 +430,8 @@ extern "C" fg_status fg_plan_pass(const fg_pass_desc* d, fg_plan** out_plan) {
       }
     }
     const bool inlaunch_ok =
-        total_items <= int64_t(kInLaunchMaxItemsPerSlot) * target_cus * kMfmaSlotsPerCu;
+        total_items <= int64_t(kInLaunchMaxItemsPerSlot) * target_cus *
+                           resident_slots_per_cu(valu_groups < int64_t(groups.size()), D, B);
     {
       int64_t n_mfma_items = 0;
       for (size_t gi = 0; gi < groups.size(); ++gi)

@@ -56,7 +56,11 @@ def check_plan(plan, spec):
         assert int(m[3]) <= 32 or gi >= n_inl
     if n_inl:
         assert n_inl == sum(1 for m in merges if int(m[3]) <= 32)
-        assert len(items) <= 4 * 2 * info["target_cus"]
+        # at most four items per resident work-group slot of the launched
+        # kernel (the slot count is checked against the device on the GPU)
+        slots = plan.resident_slots()[0]
+        assert slots in (2, 3, 4)
+        assert len(items) <= 4 * slots * info["target_cus"]
     merge_by_group = {}
     for gi, m in enumerate(merges):
         seq, kvh, row0, nrows, nsplit, slot0, pad0, pad1 = map(int, m)
