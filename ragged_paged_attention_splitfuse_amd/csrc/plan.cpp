@@ -105,6 +105,9 @@ constexpr double kSkewedSplitFactor = 2.0;
 // Measured on MI355X, the 70B-class decode half (32 GQA decodes, 64 groups):
 // 542 items on 512 slots took 34.5 us of attention; 492 items (8 splits) took
 // 28.1 us and 438 items (7 splits) 27.8 us, against 31.5 us at 546 items.
+// A round is counted as two work-groups per CU for every tile-free plan: in
+// the decode-only kernel's three, 64 decodes were fitted to three rounds
+// (2,304 items) and took 689 us of attention against 685 us unfitted.
 constexpr double kRoundFitSlack = 0.25;
 constexpr int kRoundFitPasses = 4;
 
